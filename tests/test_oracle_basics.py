@@ -1,0 +1,258 @@
+"""Pins for the oracle's generator, codebook, transforms and byte layout.
+
+Every check here compares the oracle with something other than itself: a
+published generator output, a closed form, a textbook table, a library routine
+(scipy's Hadamard, numerical quadrature), an invariant, or Monte Carlo.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, special, stats
+from scipy.linalg import hadamard
+
+from oracle import codebook, layout, rng
+from oracle.rotation import Transforms, fwht, haar_orthogonal
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_splitmix64_published_outputs():
+    g = _gold("splitmix64.json")
+    out = rng.splitmix64(g["seed"], np.arange(len(g["first_outputs_hex"])))
+    assert [format(int(v), "016x") for v in out] == g["first_outputs_hex"]
+
+
+def test_sign_vector_reproducible_and_balanced():
+    a = rng.sign_vector(42, rng.ROLE_KEY_SIGNS, 4096)
+    b = rng.sign_vector(42, rng.ROLE_KEY_SIGNS, 4096)
+    c = rng.sign_vector(42, rng.ROLE_VALUE_SIGNS, 4096)
+    assert np.array_equal(a, b)
+    assert set(np.unique(a)) == {-1.0, 1.0}
+    assert abs(a.mean()) < 4 / np.sqrt(4096)
+    assert abs((a * c).mean()) < 4 / np.sqrt(4096)        # different roles are unrelated
+
+
+def test_box_muller_is_standard_normal():
+    z = rng.gaussian(7, rng.ROLE_SKETCH_GAUSS, 400, 500).ravel()
+    assert abs(z.mean()) < 5 / np.sqrt(z.size)
+    assert abs(z.var() - 1) < 5 * np.sqrt(2 / z.size)
+    assert stats.kstest(z, "norm").pvalue > 1e-3
+    pairs = z[: z.size // 2 * 2].reshape(-1, 2)
+    assert abs(np.corrcoef(pairs.T)[0, 1]) < 5 / np.sqrt(len(pairs))
+
+
+# ---------------------------------------------------------------- codebook
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_d3_is_uniform_quantizer(bits):
+    # For d = 3 a coordinate of a uniform point on the sphere is uniform on
+    # [-1, 1] (Archimedes), whose Lloyd-Max quantizer is the uniform grid.
+    L = 1 << bits
+    c = codebook.lloyd_max(3, bits)
+    assert np.allclose(c, -1 + (2 * np.arange(L) + 1) / L, atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_codebook_one_bit_closed_form(d):
+    # One bit: the centroid is E[X | X > 0] = 2 int_0^1 x f_d = 2 / ((d-1) B(1/2, (d-1)/2)).
+    c = codebook.lloyd_max(d, 1)
+    exact = 2.0 / ((d - 1) * special.beta(0.5, (d - 1) / 2.0))
+    assert np.allclose(c, [-exact, exact], rtol=1e-13)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_gaussian_limit_matches_max_table(bits):
+    g = _gold("gaussian_lloyd_max.json")
+    d = 1 << 16
+    c = codebook.lloyd_max(d, bits) * np.sqrt(d)
+    pos = c[len(c) // 2:]
+    assert np.allclose(pos, g["positive_centroids"][str(bits)], atol=2.5e-4)
+    D = codebook.distortion(codebook.lloyd_max(d, bits), d)
+    assert abs(D - g["mse"][str(bits)]) < 1e-3 * g["mse"][str(bits)] + 6e-5
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (256, 4), (64, 2)])
+def test_codebook_centroid_and_nearest_neighbour_conditions(d, bits):
+    # Independent of the incomplete-beta path: adaptive quadrature of the pdf.
+    c = codebook.lloyd_max(d, bits)
+    t = codebook.thresholds(c)
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    f = lambda x: codebook.marginal_pdf(x, d)
+    for j in range(len(c)):
+        m, _ = integrate.quad(f, edges[j], edges[j + 1], epsabs=1e-14, epsrel=1e-12, limit=200)
+        mx, _ = integrate.quad(lambda x: x * f(x), edges[j], edges[j + 1], epsabs=1e-15, epsrel=1e-12, limit=200)
+        assert abs(mx / m - c[j]) < 1e-9
+    assert np.allclose(c, -c[::-1], atol=1e-15)
+    y = np.random.default_rng(0).normal(0, 1 / np.sqrt(d), 20000)
+    idx = np.searchsorted(t, y, side="left")
+    assert np.array_equal(idx, np.argmin(np.abs(y[:, None] - c[None, :]), axis=1))
+
+
+def test_codebook_total_mass_and_second_moment():
+    for d in (3, 64, 128, 256):
+        assert abs(codebook.marginal_cdf(1.0, d) - 1) < 1e-14
+        m2 = codebook.cell_second_moments(np.array([-1.0, 1.0]), d)[0]
+        assert abs(m2 - 1.0 / d) < 1e-14                   # E[X^2] = 1/d on the sphere
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (256, 2)])
+def test_codebook_distortion_monte_carlo(d, bits):
+    c = codebook.lloyd_max(d, bits)
+    t = codebook.thresholds(c)
+    g = np.random.default_rng(1).standard_normal((20000, d))
+    u = g / np.linalg.norm(g, axis=1, keepdims=True)        # uniform on the sphere
+    err = ((u - c[np.searchsorted(t, u, side="left")]) ** 2).sum(1)
+    mc, se = err.mean(), err.std() / np.sqrt(len(err))
+    assert abs(mc - codebook.distortion(c, d)) < 5 * se
+
+
+def test_theorem1_bound_and_printed_ratios():
+    # [README] "Paper Validation": Thm 1 holds for unit vectors and the
+    # distortion tracks 1/4^b.  The bound's constant is an image on the page;
+    # READING: sqrt(3) pi / 2.  2- and 3-bit ratios agree with the printed
+    # 0.70x / 0.82x within 0.03; the printed 0.97x at 4 bits does not follow
+    # from this constant (documented contradiction) and is only bounded.
+    g = _gold("readme_validation.json")["thm1_bound_ratio_printed"]
+    const = np.sqrt(3) * np.pi / 2
+    for bits in (1, 2, 3, 4):
+        D = codebook.distortion(codebook.lloyd_max(128, bits), 128)
+        ratio = D / (const / 4 ** bits)
+        assert ratio < 1.0
+        if str(bits) in ("2", "3"):
+            Dg = codebook.distortion(codebook.lloyd_max(1 << 16, bits), 1 << 16)
+            assert abs(Dg / (const / 4 ** bits) - g[str(bits)]) < 0.03
+
+
+def test_value_cosine_matches_readme_2bit():
+    # E cos(v, v~) -> sqrt(1 - D_b(d)) (centroid condition: <y, yhat> = ||yhat||^2 on
+    # average); the README measures 0.940 for 2-bit values at head_dim 256.
+    d = 256
+    g = _gold("readme_validation.json")
+    c = codebook.lloyd_max(d, 2)
+    closed = np.sqrt(1 - codebook.distortion(c, d))
+    assert abs(closed - g["value_cos_2bit_head_dim256"]) < 1.5e-3
+    T = Transforms(d, "fwht", 3)
+    x = np.random.default_rng(2).standard_normal((4000, d))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    y = T.rot_value(u)
+    vt = T.unrot_value(c[np.searchsorted(codebook.thresholds(c), y, side="left")])
+    cos = (u * vt).sum(1) / np.linalg.norm(vt, axis=1)
+    assert abs(cos.mean() - closed) < 2e-3
+
+
+# ---------------------------------------------------------------- transforms
+
+@pytest.mark.parametrize("d", [2, 16, 128, 256])
+def test_fwht_is_sylvester_hadamard(d):
+    x = np.random.default_rng(d).standard_normal((7, d))
+    assert np.allclose(fwht(x), x @ hadamard(d).T, atol=1e-12)
+
+
+@pytest.mark.parametrize("rot,d", [("fwht", 128), ("fwht", 256), ("dense", 128), ("dense", 64)])
+def test_rotations_orthogonal_and_invertible(rot, d):
+    T = Transforms(d, rot, 11)
+    for M in (T.key_matrix(), T.value_matrix()):
+        assert np.abs(M @ M.T - np.eye(d)).max() < 1e-12
+    x = np.random.default_rng(3).standard_normal((5, d))
+    assert np.allclose(T.unrot_key(T.rot_key(x)), x, atol=1e-12)
+    assert np.allclose(T.unrot_value(T.rot_value(x)), x, atol=1e-12)
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    assert np.allclose(np.linalg.norm(T.rot_key(u), axis=1), 1.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_fwht_spreads_basis_vector(d):
+    # [Reconstruction] section 13 golden vector: the canonical basis vector is
+    # spread to magnitude 1/sqrt(d) in every coordinate.
+    T = Transforms(d, "fwht", 5)
+    y = T.rot_key(np.eye(d)[:1])[0]
+    assert np.allclose(np.abs(y), 1 / np.sqrt(d), atol=1e-15)
+
+
+def test_dense_rotation_is_the_positive_diagonal_qr_factor():
+    # Q R = A with R upper triangular and diag(R) > 0 determines Q uniquely.
+    d = 64
+    A = rng.gaussian(9, rng.ROLE_KEY_GAUSS, d, d)
+    Q = haar_orthogonal(9, rng.ROLE_KEY_GAUSS, d)
+    R = Q.T @ A
+    assert np.abs(np.tril(R, -1)).max() < 1e-12
+    assert (np.diag(R) > 0).all()
+
+
+def test_dense_rotation_coordinates_have_variance_one_over_d():
+    d = 32
+    u = np.ones(d) / np.sqrt(d)
+    ys = np.stack([Transforms(d, "dense", s).rot_key(u[None])[0] for s in range(600)])
+    assert abs((ys ** 2).mean() - 1 / d) < 4 * np.sqrt(2 / (600 * d)) / d * 3
+
+
+@pytest.mark.parametrize("rot,d", [("fwht", 128), ("dense", 128)])
+def test_sketch_transpose_and_row_norms(rot, d):
+    T = Transforms(d, rot, 13)
+    S = T.sketch_matrix()
+    a, b = np.random.default_rng(4).standard_normal((2, 3, d))
+    assert np.allclose((T.sketch(a) * b).sum(1), (a * T.sketch_t(b)).sum(1), atol=1e-9)
+    if rot == "fwht":
+        assert np.abs(S @ S.T - d * np.eye(d)).max() < 1e-10
+    else:
+        assert abs(np.diag(S @ S.T).mean() / d - 1) < 0.05
+
+
+# ---------------------------------------------------------------- layout
+
+def test_record_sizes_match_storage_formula():
+    for case in _gold("storage_formula.json")["cases"]:
+        P = 16
+        kb = layout.key_block_bytes(case["d"], case["key_bits"], P)
+        vb = layout.value_block_bytes(case["d"], case["value_bits"], P)
+        assert kb == P * case["key_record_bytes"]
+        assert vb == P * case["value_record_bytes"]
+        assert kb % 16 == 0 and vb % 16 == 0
+
+
+@pytest.mark.parametrize("d,m,bv", [(128, 2, 2), (128, 3, 4), (256, 2, 2), (256, 3, 3)])
+def test_pack_unpack_roundtrip(d, m, bv):
+    g = np.random.default_rng(d + m)
+    shape = (3, 2, 16, d)
+    codes = g.integers(0, 1 << m, shape)
+    z = g.integers(0, 2, shape).astype(bool)
+    nu = g.random((3, 2, 16)).astype(np.float32)
+    gam = g.random((3, 2, 16)).astype(np.float32)
+    buf = layout.pack_key_block(codes, z, nu, gam, m)
+    assert buf.shape[-1] == layout.key_block_bytes(d, m + 1)
+    c2, z2, n2, g2 = layout.unpack_key_block(buf, d, m)
+    assert np.array_equal(c2, codes) and np.array_equal(z2, z)
+    assert np.array_equal(n2, nu) and np.array_equal(g2, gam)
+    vcodes = g.integers(0, 1 << bv, shape)
+    vbuf = layout.pack_value_block(vcodes, nu, bv)
+    assert vbuf.shape[-1] == layout.value_block_bytes(d, bv)
+    vc2, vn2 = layout.unpack_value_block(vbuf, d, bv)
+    assert np.array_equal(vc2, vcodes) and np.array_equal(vn2, nu)
+
+
+def test_layout_bit_positions_by_hand():
+    d, m = 128, 2
+    codes = np.zeros((16, d), int)
+    z = np.zeros((16, d), bool)
+    codes[3, 37] = 2          # plane 1, token 3, coordinate 37
+    z[5, 100] = True          # QJL plane, token 5, coordinate 100
+    buf = layout.pack_key_block(codes, z, np.zeros(16), np.zeros(16), m)
+    plane = 16 * d // 8
+    nz = np.flatnonzero(buf)
+    assert list(nz) == [plane + 3 * 16 + 37 // 8, 2 * plane + 5 * 16 + 100 // 8]
+    assert buf[plane + 3 * 16 + 4] == 1 << (37 % 8)
+    vcodes = np.zeros((16, d), int)
+    vcodes[9, 70] = 3         # both planes, slot 9, coordinate 70
+    vbuf = layout.pack_value_block(vcodes, np.zeros(16), 2)
+    vplane = d * 2
+    assert list(np.flatnonzero(vbuf)) == [70 * 2 + 1, vplane + 70 * 2 + 1]
+    assert vbuf[70 * 2 + 1] == 1 << (9 - 8)
