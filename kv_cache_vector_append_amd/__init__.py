@@ -1,0 +1,21 @@
+"""TurboQuant-style compressed KV cache for AMD Instinct MI355X (gfx950).
+
+The work happens in the HIP library ``libtq_hip.so`` behind the C ABI of
+``include/tq.h``; this package only marshals torch tensors into those calls.
+"""
+from ._lib import (  # noqa: F401
+    CacheBuffers,
+    Config,
+    TQError,
+    allocate_cache,
+    decode_attention,
+    decode_workspace_bytes,
+    dequantize,
+    exported_symbols,
+    init_codebooks,
+    key_block_bytes,
+    load_library,
+    params_bytes,
+    quantize_append,
+    value_block_bytes,
+)

@@ -1,0 +1,125 @@
+// Internal definitions shared by the host code and the HIP kernels of the
+// library: the parameter-blob layout and the argument blocks of each launch.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tqi {
+
+// ---------------------------------------------------------------------------
+// Parameter blob (written by tq_init_codebooks, read by every kernel).
+//   [0, 64)        header (int32/uint64 fields below)
+//   [64, 128)      key centroids, float[16] ascending (2^(key_bits-1) used)
+//   [128, 192)     key thresholds, float[16] (midpoints; unused = +inf)
+//   [192, 256)     value centroids, float[16]
+//   [256, 320)     value thresholds, float[16]
+//   [320, 384)     key bit-plane coefficients, float[16] (see below)
+//   [384, 448)     value bit-plane coefficients, float[16]
+//   [1024, 1280)   Rademacher sign words, 4 roles x 64 bytes (coordinate i of a
+//                  role is bit i % 32 of uint32 word i / 32; 1 means -1)
+//   [2048, ...)    dense variant: Pi_K, G, Pi_V as float[d*d] row-major each
+//
+// Bit-plane coefficients: a symmetric (odd) codebook c over b-bit codes is a
+// multilinear function of the signs s_k = 1 - 2*bit_k(idx):
+//   c[idx] = sum_{S odd} a_S prod_{k in S} s_k,   a_S = 2^-b sum_idx c[idx] prod_{k in S} s_k.
+// a_S is stored at index S (bitmask); even subsets are zero.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kParamsMagic = 0x31505154u;  // "TQP1"
+constexpr int kOffKeyCentroids = 64;
+constexpr int kOffKeyThresholds = 128;
+constexpr int kOffValueCentroids = 192;
+constexpr int kOffValueThresholds = 256;
+constexpr int kOffKeyPlaneCoef = 320;
+constexpr int kOffValuePlaneCoef = 384;
+constexpr int kOffSigns = 1024;
+constexpr int kSignRoleBytes = 64;
+constexpr int kOffDense = 2048;
+
+enum SignRole { kRoleKeyRot = 0, kRoleSketch1 = 1, kRoleSketch2 = 2, kRoleValueRot = 3 };
+
+struct ParamsHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t head_dim;
+  int32_t key_mse_bits;
+  int32_t value_bits;
+  int32_t rotation;
+  uint64_t seed;
+  uint32_t total_bytes;
+  uint32_t reserved[7];
+};
+static_assert(sizeof(ParamsHeader) == 64, "header is 64 bytes");
+
+inline size_t params_bytes(int d, int rotation) {
+  return kOffDense + (rotation == TQ_ROT_DENSE ? size_t(3) * d * d * sizeof(float) : 0);
+}
+inline size_t key_block_bytes(int d, int key_bits, int P) { return size_t(key_bits) * P * d / 8 + 8 * size_t(P); }
+inline size_t value_block_bytes(int d, int value_bits, int P) { return size_t(value_bits) * P * d / 8 + 4 * size_t(P); }
+
+// ---------------------------------------------------------------------------
+// Launch argument blocks.
+// ---------------------------------------------------------------------------
+struct CacheView {
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  const int32_t* block_table;
+  uint16_t* k_window;  // fp16 bits
+  uint16_t* v_window;
+  int32_t num_pages, max_seqs, max_pages_per_seq;
+  int32_t num_kv_heads, page_tokens, window;
+  int32_t key_block, value_block;  // bytes
+};
+
+struct AppendArgs {
+  CacheView cache;
+  const uint8_t* params;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_slots;
+  const int32_t* ctx_len_before;
+  const int32_t* cu_new_tokens;
+  int32_t num_seqs, dtype, key_mse_bits, value_bits;
+  int32_t parts;  // workers per (sequence, kv head)
+};
+
+struct DecodeArgs {
+  CacheView cache;
+  const uint8_t* params;
+  const void* q;
+  const int32_t* seq_slots;
+  const int32_t* ctx_len;
+  float* out;
+  float* workspace;   // [num_seqs][H_q][splits][2 + 2d]
+  float* logits;      // optional [num_seqs][H_q][max_ctx]
+  int32_t num_seqs, num_q_heads, q_dtype, key_mse_bits, value_bits;
+  int32_t splits, split_tokens, max_ctx;
+  float scale;
+};
+
+struct DequantArgs {
+  CacheView cache;
+  const uint8_t* params;
+  float* k_out;
+  float* v_out;
+  int32_t seq_slot, tok_begin, tok_end, key_mse_bits, value_bits;
+};
+
+// Decode split sizing shared by the workspace query and the launch.
+struct SplitPlan {
+  int splits;
+  int split_tokens;
+};
+SplitPlan plan_splits(int d, int num_seqs, int num_kv_heads, int max_ctx);
+
+// Host-side parameter construction (tq_host.cpp).
+void build_params(const tq_config& cfg, uint8_t* blob);
+
+// Kernel launchers (one per .hip file); return hipError_t as int.
+int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream);
+int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
+int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);
+
+}  // namespace tqi

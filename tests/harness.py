@@ -1,0 +1,207 @@
+"""Test harness: runs the HIP library and the oracle on the same seeded inputs
+and compares them under the parity rules.
+
+Parity rules (from the acceptance criteria of this build):
+  * codes and QJL bits are bit-exact, except a code whose pre-quantization
+    coordinate lies within 1e-6 of a threshold (counted, reported); for a token
+    with such a flip, the QJL bits are re-derived from the GPU's codes, and a
+    bit may differ only where |w_j| / sqrt(d) < 1e-6;
+  * fp32 norms agree to a relative 1e-5 (fp32 vs fp64 arithmetic);
+  * the fp16 window is bit-exact;
+  * decode: max over (seq, head) rows of max|o_gpu - o_ref| / max|o_ref| <= 2e-3.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import workloads
+from oracle import tq
+
+BAND = 1e-6
+NORM_RTOL = 1e-5
+DECODE_TOL = 2e-3
+
+
+def lib():
+    import kv_cache_vector_append_amd as tqa
+    return tqa
+
+
+def oracle_config(w: workloads.Workload) -> tq.Config:
+    return tq.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
+                     w.window, w.rotation, w.method_seed)
+
+
+def lib_config(w: workloads.Workload):
+    return lib().Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
+                        w.window, w.rotation, w.method_seed)
+
+
+@dataclass
+class Run:
+    w: workloads.Workload
+    lens: list
+    cfg: object
+    params: torch.Tensor
+    cache: object
+    ocfg: tq.Config
+    P: tq.Params
+    ocache: tq.Cache
+    K: list = field(default_factory=list)   # per sequence, CPU tensors [len, H, d]
+    V: list = field(default_factory=list)
+    block_table: np.ndarray | None = None
+
+
+def make_run(w: workloads.Workload, lens, chunks=1, oracle_append=True, device="cuda", P=None):
+    """Append `lens[i]` tokens to sequence i on the GPU (in `chunks` calls) and in the oracle."""
+    tqa = lib()
+    cfg = lib_config(w)
+    ocfg = oracle_config(w)
+    nseq = len(lens)
+    mpp = max(1, -(-max(max(lens), 1) // w.page_tokens))
+    bt = workloads.block_table(w, nseq, mpp).numpy()
+    params = torch.empty(tqa.params_bytes(cfg), dtype=torch.uint8, device=device)
+    tqa.init_codebooks(cfg, params)
+    cache = tqa.allocate_cache(cfg, nseq * mpp, torch.from_numpy(bt), device)
+    P = P if P is not None else tq.Params(ocfg)
+    ocache = tq.Cache(ocfg, nseq * mpp, bt)
+    K = [workloads.kv_tokens(w, "k", s, 0, n) for s, n in enumerate(lens)]
+    V = [workloads.kv_tokens(w, "v", s, 0, n) for s, n in enumerate(lens)]
+    done = [0] * nseq
+    for c in range(chunks):
+        ks, vs, cu, before = [], [], [0], []
+        for s, n in enumerate(lens):
+            hi = n if c == chunks - 1 else (n * (c + 1)) // chunks
+            ks.append(K[s][done[s]:hi]); vs.append(V[s][done[s]:hi])
+            before.append(done[s]); cu.append(cu[-1] + hi - done[s]); done[s] = hi
+        kn = torch.cat(ks).to(device).contiguous()
+        vn = torch.cat(vs).to(device).contiguous()
+        if kn.shape[0] == 0:
+            continue
+        i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
+        maxn = max(cu[i + 1] - cu[i] for i in range(nseq))
+        tqa.quantize_append(cfg, params, cache, kn, vn, i32(list(range(nseq))), i32(before), i32(cu), maxn)
+        if oracle_append:
+            tq.append(P, ocache, torch.cat(ks).double().numpy(), torch.cat(vs).double().numpy(),
+                      np.arange(nseq), before, cu)
+    torch.cuda.synchronize()
+    return Run(w, list(lens), cfg, params, cache, ocfg, P, ocache, K, V, bt)
+
+
+def gpu_cache_as_oracle(run: Run) -> tq.Cache:
+    """The GPU's bytes, decoded with the oracle's layout reader."""
+    c = tq.Cache(run.ocfg, run.cache.k_pages.shape[0], run.block_table)
+    kw = run.cache.k_window.cpu().numpy().view(np.float16) if run.cache.k_window is not None else None
+    vw = run.cache.v_window.cpu().numpy().view(np.float16) if run.cache.v_window is not None else None
+    c.load_bytes(run.cache.k_pages.cpu().numpy(), run.cache.v_pages.cpu().numpy(), kw, vw)
+    return c
+
+
+@dataclass
+class AppendReport:
+    tokens: int = 0
+    key_code_flips: int = 0
+    value_code_flips: int = 0
+    qjl_band_flips: int = 0
+    unexcused: int = 0
+    max_nu_rel: float = 0.0
+    max_gamma_rel: float = 0.0
+    window_mismatch: int = 0
+    notes: list = field(default_factory=list)
+
+
+def _near_threshold(y, t):
+    return np.min(np.abs(y[..., None] - np.asarray(t)[None, :]), axis=-1) < BAND if len(t) else np.zeros(y.shape, bool)
+
+
+def compare_append(run: Run, gc: tq.Cache | None = None, positions=None) -> AppendReport:
+    """Compare GPU pages with the oracle's encoding of the same inputs."""
+    gc = gc if gc is not None else gpu_cache_as_oracle(run)
+    P, d, H = run.P, run.ocfg.head_dim, run.ocfg.num_kv_heads
+    rep = AppendReport()
+    for s, n in enumerate(run.lens):
+        pos = np.arange(n) if positions is None else np.asarray(positions[s])
+        if len(pos) == 0:
+            continue
+        g = gc.gather(s, pos)
+        kx = run.K[s][pos].double().numpy().reshape(-1, d)
+        vx = run.V[s][pos].double().numpy().reshape(-1, d)
+        ek = tq.encode_keys(P, kx)
+        ev = tq.encode_values(P, vx)
+        rep.tokens += len(pos) * H
+        gk = g["k_codes"].reshape(-1, d).astype(np.int64)
+        gz = g["k_z"].reshape(-1, d)
+        # key codes
+        mism = gk != ek["codes"]
+        near = _near_threshold(ek["y"], P.kt)
+        rep.unexcused += int((mism & ~near).sum())
+        rep.key_code_flips += int((mism & near).sum())
+        flipped_tok = mism.any(axis=1)
+        # QJL bits: re-derive from the GPU's codes where a code flipped
+        e = ek["y"] - P.kc[gk]
+        w = np.where(flipped_tok[:, None], P.T.sketch(e), ek["w"])
+        zexp = w < 0
+        zero = ek["nu"] == 0
+        zexp[zero] = False
+        zm = gz != zexp
+        zband = np.abs(w) / np.sqrt(d) < BAND
+        rep.unexcused += int((zm & ~zband).sum())
+        rep.qjl_band_flips += int((zm & zband).sum())
+        # norms
+        gnu = g["k_nu"].reshape(-1).astype(np.float64)
+        ggam = g["k_gamma"].reshape(-1).astype(np.float64)
+        onu = ek["nu"]
+        ogam = np.where(zero, 0.0, np.linalg.norm(e, axis=1))
+        rep.max_nu_rel = max(rep.max_nu_rel, float(np.max(np.abs(gnu - onu) / np.maximum(onu, 1e-30))))
+        rep.max_gamma_rel = max(rep.max_gamma_rel, float(np.max(np.abs(ggam - ogam) / np.maximum(ogam, 1e-30))))
+        # value codes
+        gv = g["v_codes"].reshape(-1, d).astype(np.int64)
+        vm = gv != ev["codes"]
+        vnear = _near_threshold(ev["y"], P.vt)
+        rep.unexcused += int((vm & ~vnear).sum())
+        rep.value_code_flips += int((vm & vnear).sum())
+        gvn = g["v_nu"].reshape(-1).astype(np.float64)
+        rep.max_nu_rel = max(rep.max_nu_rel, float(np.max(np.abs(gvn - ev["nu"]) / np.maximum(ev["nu"], 1e-30))))
+        # fp16 window
+        W = run.ocfg.window
+        if W and positions is None:
+            wpos = np.arange(max(0, n - W), n)
+            for hh in range(H):
+                exp_k = run.K[s][wpos, hh].double().numpy().astype(np.float16)
+                exp_v = run.V[s][wpos, hh].double().numpy().astype(np.float16)
+                got_k = gc.k_window[s, hh, wpos % W]
+                got_v = gc.v_window[s, hh, wpos % W]
+                rep.window_mismatch += int((exp_k.view(np.uint16) != got_k.view(np.uint16)).sum())
+                rep.window_mismatch += int((exp_v.view(np.uint16) != got_v.view(np.uint16)).sum())
+    return rep
+
+
+def gpu_decode(run: Run, q: torch.Tensor, lens=None, want_logits=False, scale=0.0):
+    tqa = lib()
+    lens = run.lens if lens is None else lens
+    nseq = q.shape[0]
+    max_ctx = max(max(lens), 1)
+    dev = run.params.device
+    ws = torch.empty(tqa.decode_workspace_bytes(run.cfg, nseq, max_ctx) // 4 + 4, dtype=torch.float32, device=dev)
+    out = torch.empty((nseq, run.w.num_q_heads, run.w.head_dim), dtype=torch.float32, device=dev)
+    logits = torch.full((nseq, run.w.num_q_heads, max_ctx), float("nan"), device=dev) if want_logits else None
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    tqa.decode_attention(run.cfg, run.params, run.cache, q.to(dev).contiguous(), i32(list(range(nseq))),
+                         i32(list(lens)), max_ctx, out, ws, scale, logits)
+    torch.cuda.synchronize()
+    return (out.cpu().double().numpy(), logits.cpu().double().numpy() if want_logits else None)
+
+
+def decode_error(o_gpu, o_ref):
+    """max over rows of max|o_gpu - o_ref| / max|o_ref| (rows with zero reference must be exactly zero)."""
+    num = np.abs(o_gpu - o_ref).max(axis=-1)
+    den = np.abs(o_ref).max(axis=-1)
+    err = np.where(den > 0, num / np.maximum(den, 1e-300), num)
+    return float(err.max())
+
+
+def queries(w: workloads.Workload, nseq: int):
+    return torch.stack([workloads.queries(w, s) for s in range(nseq)])
