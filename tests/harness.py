@@ -179,6 +179,54 @@ def compare_append(run: Run, gc: tq.Cache | None = None, positions=None) -> Appe
     return rep
 
 
+def aligned_oracle_cache(run: Run, gc: tq.Cache | None = None):
+    """The oracle's own cache, except that where the GPU took the other side of a
+    near-threshold (|y - t| < 1e-6) code decision, the oracle adopts the GPU's codes
+    and recomputes that token's residual norm and QJL bits itself in float64.
+
+    Returns (cache, number of token-heads adjusted).  An end-to-end decode over
+    this cache is the oracle's result under the same band decisions; without it
+    one excused flip on a token holding much of the softmax mass can move the
+    output far more than the decode tolerance.
+    """
+    import copy
+    gc = gc if gc is not None else gpu_cache_as_oracle(run)
+    oc = copy.deepcopy(run.ocache)
+    P, d = run.P, run.ocfg.head_dim
+    adjusted = 0
+    for s, n in enumerate(run.lens):
+        if n == 0:
+            continue
+        pos = np.arange(n)
+        pg, t = oc.locate(s, pos)
+        g = gc.gather(s, pos)
+        o = oc.gather(s, pos)
+        km = (g["k_codes"] != o["k_codes"]).any(axis=-1)          # [n, H]
+        for (i, h) in np.argwhere(km):
+            x = run.K[s][i, h].double().numpy()[None]
+            ek = tq.encode_keys(P, x)
+            codes = g["k_codes"][i, h].astype(np.int64)
+            near = np.min(np.abs(ek["y"][0][:, None] - P.kt[None, :]), axis=-1) < BAND
+            if not np.all((codes == ek["codes"][0]) | near):
+                continue                                           # a real mismatch stays visible
+            e = ek["y"][0] - P.kc[codes]
+            w = P.T.sketch(e[None])[0]
+            oc.k_codes[pg[i], h, t[i]] = codes
+            oc.k_z[pg[i], h, t[i]] = w < 0
+            oc.k_gamma[pg[i], h, t[i]] = np.float32(np.linalg.norm(e))
+            adjusted += 1
+        vm = (g["v_codes"] != o["v_codes"]).any(axis=-1)
+        for (i, h) in np.argwhere(vm):
+            ev = tq.encode_values(P, run.V[s][i, h].double().numpy()[None])
+            codes = g["v_codes"][i, h].astype(np.int64)
+            near = np.min(np.abs(ev["y"][0][:, None] - P.vt[None, :]), axis=-1) < BAND
+            if not np.all((codes == ev["codes"][0]) | near):
+                continue
+            oc.v_codes[pg[i], h, t[i]] = codes
+            adjusted += 1
+    return oc, adjusted
+
+
 def gpu_decode(run: Run, q: torch.Tensor, lens=None, want_logits=False, scale=0.0):
     tqa = lib()
     lens = run.lens if lens is None else lens
