@@ -154,25 +154,29 @@ def outlier_channels(w: Workload) -> torch.Tensor:
     return torch.stack(rows)
 
 
-def _block(w: Workload, which: str, seq: int, blk: int) -> torch.Tensor:
-    """One GEN_BLOCK x H_kv x d float64 block of raw draws for sequence `seq`."""
-    g = _gen(w.input_seed, _STREAM_K if which == "k" else _STREAM_V, seq, blk)
-    shape = (GEN_BLOCK, w.num_kv_heads, w.head_dim)
+def _draw(w: Workload, which: str, shape, g: torch.Generator, device="cpu") -> torch.Tensor:
+    """float64 draws [n, H_kv, d] with the workload's distribution for keys or values."""
     dist = w.k_dist if which == "k" else w.v_dist
-    x = torch.randn(shape, generator=g, dtype=torch.float64)
+    x = torch.randn(shape, generator=g, dtype=torch.float64, device=device)
     if dist == "normal_head_scale":
-        x = x * head_scales(w, which).view(1, -1, 1)
+        x = x * head_scales(w, which).to(device).view(1, -1, 1)
     elif dist == "normal_outlier":
         ch = outlier_channels(w)
         scale = torch.ones(w.num_kv_heads, w.head_dim, dtype=torch.float64)
         scale.scatter_(1, ch, w.outlier_scale)
-        x = x * scale.view(1, w.num_kv_heads, w.head_dim)
+        x = x * scale.to(device).view(1, w.num_kv_heads, w.head_dim)
     elif dist == "student_t3":
-        chi2 = (torch.randn((3,) + shape, generator=g, dtype=torch.float64) ** 2).sum(0)
+        chi2 = (torch.randn((3,) + tuple(shape), generator=g, dtype=torch.float64, device=device) ** 2).sum(0)
         x = x / torch.sqrt(chi2 / 3.0)
     elif dist != "normal":
         raise ValueError(dist)
     return x
+
+
+def _block(w: Workload, which: str, seq: int, blk: int) -> torch.Tensor:
+    """One GEN_BLOCK x H_kv x d float64 block of raw draws for sequence `seq`."""
+    g = _gen(w.input_seed, _STREAM_K if which == "k" else _STREAM_V, seq, blk)
+    return _draw(w, which, (GEN_BLOCK, w.num_kv_heads, w.head_dim), g)
 
 
 def kv_tokens(w: Workload, which: str, seq: int, start: int, count: int) -> torch.Tensor:
@@ -205,3 +209,25 @@ def block_table(w: Workload, num_seqs: int, pages_per_seq: int, salt: int = 0) -
     """[num_seqs, pages_per_seq] int32 physical ids, every page used once, in shuffled order."""
     perm = page_permutation(w, num_seqs * pages_per_seq, salt)
     return perm.view(num_seqs, pages_per_seq).contiguous()
+
+
+def device_generator(w: Workload, salt: int, device) -> torch.Generator:
+    """A seeded generator on `device` for benchmark-scale draws."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(w.input_seed) * 1000003 + salt)
+    return g
+
+
+def device_kv(w: Workload, which: str, num_tokens: int, g: torch.Generator, device) -> torch.Tensor:
+    """Benchmark-scale keys or values [num_tokens, H_kv, d] drawn on the device.
+
+    Same distribution recipe as ``kv_tokens`` (a different random stream), so
+    gigabytes of inputs never pass through host memory.
+    """
+    x = _draw(w, which, (num_tokens, w.num_kv_heads, w.head_dim), g, device)
+    return x.to(w.torch_dtype).contiguous()
+
+
+def device_queries(w: Workload, num_seqs: int, g: torch.Generator, device) -> torch.Tensor:
+    x = torch.randn((num_seqs, w.num_q_heads, w.head_dim), generator=g, dtype=torch.float64, device=device)
+    return x.to(w.torch_dtype).contiguous()
