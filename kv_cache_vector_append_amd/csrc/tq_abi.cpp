@@ -201,7 +201,8 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
   a.split_tokens = p.split_tokens;
   a.max_ctx = mc;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
-  const int e = tqi::launch_decode(*cfg, a, stream);
+  const int e = tqi::decode_mfma_supported(*cfg) ? tqi::launch_decode_mfma(*cfg, a, stream)
+                                                 : tqi::launch_decode(*cfg, a, stream);
   if (e != 0) return hip_fail(e, "decode launch");
   return TQ_OK;
 }

@@ -120,6 +120,8 @@ void build_params(const tq_config& cfg, uint8_t* blob);
 // Kernel launchers (one per .hip file); return hipError_t as int.
 int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream);
 int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
+bool decode_mfma_supported(const tq_config& cfg);
+int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);
 
 }  // namespace tqi

@@ -1,0 +1,80 @@
+// Building blocks of the matrix-core (MFMA) decode on gfx950.
+//
+// The decode contractions -- query x decoded keys for the GQA group, and
+// softmax weights x decoded values -- run on v_mfma_scale_f32_16x16x128_f8f6f4
+// with one operand in fp4 (e2m1) and the other in fp8 (e4m3, OCP encoding):
+//
+//  * Every code bit-plane maps to a +-1 fp4 operand: a symmetric Lloyd-Max
+//    codebook is an odd function of the code's sign bits s_k = 1 - 2 bit_k,
+//    c[idx] = sum over odd subsets S of a_S prod_{k in S} s_k, so a dot
+//    product with decoded codes is a weighted sum of +-1 plane products, and
+//    the QJL bits are +-1 already.  Bits turn into fp4 nibbles with two ALU
+//    operations per 8 values.
+//  * The fp32 operand (rotated query, softmax weight) is split into four fp8
+//    parts x = sum_p 16^-p x_p held in four operand rows; the fp32 accumulator
+//    then carries about 2^-17 relative precision, far below the fp32 -> fp64
+//    parity tolerance.
+//
+// Register layouts of the 16x16x128 f8f6f4 MFMA on gfx950 (lane l, group
+// g = l / 16, index r = l % 16; measured on the device):
+//   fp8 operand:  32 bytes per lane; byte e holds K index 16g + e (e < 16) or
+//                 64 + 16g + (e - 16) (e >= 16); row/column r.
+//   fp4 operand:  16 bytes per lane; nibble e (low nibble first) holds K index
+//                 32g + e; row/column r.
+//   result:       4 floats per lane; float i holds row 4g + i, column r.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tqi {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtFp8 = 0;
+constexpr int kFmtFp4 = 4;
+constexpr int kScaleOne = 127;  // E8M0 exponent of 1.0
+
+// acc += A(fp8) x B(fp4)
+__device__ __forceinline__ v4f mfma_f8_f4(const v8i& a, const v8i& b, v4f acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp8, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+}
+
+// acc += A(fp4) x B(fp8)
+__device__ __forceinline__ v4f mfma_f4_f8(const v8i& a, const v8i& b, v4f acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp4, kFmtFp8, 0, kScaleOne, 0, kScaleOne);
+}
+
+// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0).  Output dword j, nibble
+// n holds bit 4n + j of w, so fp4 element e = 8j + n comes from bit
+// 4(e % 8) + e / 8.
+__device__ __forceinline__ void bits_to_fp4_pm1(uint32_t w, v8i& out) {
+  out[0] = int(((w << 3) & 0x88888888u) | 0x22222222u);
+  out[1] = int(((w << 2) & 0x88888888u) | 0x22222222u);
+  out[2] = int(((w << 1) & 0x88888888u) | 0x22222222u);
+  out[3] = int((w & 0x88888888u) | 0x22222222u);
+}
+
+// Bit position inside a 32-bit source word of fp4 element e (inverse of the above).
+__host__ __device__ constexpr int fp4_elem_bit(int e) { return 4 * (e % 8) + e / 8; }
+
+// K index held by byte e of an fp8 operand in lane group g.
+__host__ __device__ constexpr int fp8_elem_k(int g, int e) { return e < 16 ? 16 * g + e : 64 + 16 * g + (e - 16); }
+
+// Four-part fp8 split of x (|x| <= 448): bytes p0 | p1 << 8 | p2 << 16 | p3 << 24
+// with x ~= p0 + p1/16 + p2/256 + p3/4096, each part rounded to nearest even.
+__device__ __forceinline__ uint32_t fp8_split4(float x) {
+  uint32_t out = 0;
+  float r = x;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false);
+    const float back = __builtin_amdgcn_cvt_f32_fp8(packed, 0);
+    out |= uint32_t(packed & 0xff) << (8 * p);
+    r = (r - back) * 16.0f;
+  }
+  return out;
+}
+
+}  // namespace tqi

@@ -25,7 +25,17 @@ CASES = {
     "hd256_long_fwht_3_2": ([257, 31], 1),
     "outlier_stress": ([520, 260, 1], 1),
     "mixed_serving": ([400, 3, 160, 0], 3),
+    # shapes outside the matrix-core kernel (head_dim 64, GQA group of 8) use the plain kernels
+    "plain_hd64_gqa8": ([300, 130], 2),
+    "plain_hd128_gqa8": ([200, 50], 1),
 }
+
+import workloads as _w
+_w.WORKLOADS.setdefault("plain_hd64_gqa8", _w.GQA_DECODE.replace(
+    name="plain_hd64_gqa8", num_q_heads=16, num_kv_heads=2, head_dim=64, key_bits=3, value_bits=3, window=32))
+_w.WORKLOADS.setdefault("plain_hd128_gqa8", _w.GQA_DECODE.replace(
+    name="plain_hd128_gqa8", num_q_heads=16, num_kv_heads=2, key_bits=4, value_bits=2, window=48,
+    rotation="dense"))
 
 _RUNS = {}
 _PARAMS = {}
