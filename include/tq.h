@@ -73,14 +73,17 @@ typedef struct {
 
 /* The paged cache.  Page layout per (page, KV head) block, all little-endian
  * ([Design Study] "Packed format and complete bit accounting";
- * [Reconstruction] section 8 "Bit Accounting and Memory Formulas"):
- *   key block   = (key_bits-1) code bit-planes, then one QJL sign plane, each
- *                 page_tokens rows of head_dim/8 bytes (row t: bit k of byte
- *                 j belongs to coordinate 8j+k); then nu[page_tokens] float32;
- *                 then gamma[page_tokens] float32 (residual norms).
- *   value block = value_bits code bit-planes, each head_dim rows of
- *                 page_tokens/8 bytes (row i: bit t = token slot t of
- *                 coordinate i); then nu[page_tokens] float32.
+ * [Reconstruction] section 8 "Bit Accounting and Memory Formulas").  Codes
+ * are bit-sliced, lowest code bit first, in 32-bit words; m = key_bits - 1:
+ *   key block   = for token slot t, for 32-coordinate group g, for plane j in
+ *                 0..m: one word whose bit k belongs to coordinate 32g+k
+ *                 (planes 0..m-1 code bits, plane m the QJL sign bits);
+ *                 then (nu_t, gamma_t) float32 pairs for t = 0..page_tokens-1
+ *                 (input norm, residual norm).
+ *   value block = for coordinate pair i, for plane j in 0..value_bits-1: one
+ *                 word whose bits 0..15 are plane j of slots 0..15 of
+ *                 coordinate 2i and bits 16..31 the same for coordinate 2i+1;
+ *                 then nu[page_tokens] float32.
  * A QJL bit is 1 where the projected residual is negative.  Bytes of slots at
  * or beyond a sequence's length are unspecified. */
 typedef struct {

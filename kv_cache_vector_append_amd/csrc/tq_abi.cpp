@@ -160,7 +160,9 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
 size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t max_ctx) {
   if (check_config(cfg) != TQ_OK || num_seqs <= 0 || max_ctx < 0) return 0;
   const tqi::SplitPlan p = tqi::plan_splits(cfg->head_dim, num_seqs, cfg->num_kv_heads, max_ctx > 0 ? max_ctx : 1);
-  return size_t(num_seqs) * cfg->num_q_heads * p.splits * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
+  const size_t partials =
+      size_t(num_seqs) * cfg->num_q_heads * (p.splits + 1) * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
+  return tqi::decode_prep_bytes(cfg->head_dim, num_seqs, cfg->num_kv_heads) + partials;
 }
 
 tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, const tq_cache* cache, const void* q,

@@ -172,21 +172,28 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const float gamma = sqrtf(es);
       sketch<D, ROT>(e, a.params, lds, lane);
       if (page_ok) {
-        uint8_t* row = kb + size_t(t) * (D / 8);
-        for (int p = 0; p <= mk; ++p) {
-          uint32_t word = 0;
+        // token row: for each 32-coordinate group, the words of all planes
+        uint32_t words[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) words[p] = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (p > mk) break;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const bool bit = (p < mk) ? (((idx[r] >> p) & 1) != 0) : (!zero && e[r] < 0.f);
             const uint64_t m = __ballot(bit);
-            if ((lane >> 1) == r) word = (lane & 1) ? uint32_t(m >> 32) : uint32_t(m);
+            if ((lane >> 1) == r) words[p] = (lane & 1) ? uint32_t(m >> 32) : uint32_t(m);
           }
-          if (lane < D / 32) reinterpret_cast<uint32_t*>(row + size_t(p) * plane_bytes)[lane] = word;
+        }
+        if (lane < D / 32) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * (D / 32) * (mk + 1) * 4) + lane * (mk + 1);
+          for (int p = 0; p <= mk; ++p) dst[p] = words[p];
         }
         if (lane == 0) {
-          float* norms = reinterpret_cast<float*>(kb + size_t(mk + 1) * plane_bytes);
-          norms[t] = zero ? 0.f : nu;
-          norms[P + t] = zero ? 0.f : gamma;
+          float* norms = reinterpret_cast<float*>(kb + size_t(mk + 1) * plane_bytes) + 2 * t;
+          norms[0] = zero ? 0.f : nu;
+          norms[1] = zero ? 0.f : gamma;
         }
       }
       if (in_window) {
@@ -224,15 +231,22 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       }
     }
     if (page_ok) {
-      // token bits below `lo` were written by earlier calls; keep them
-      const uint32_t keep = (1u << (lo - pg * P)) - 1u;
+      // token bits below `lo` were written by earlier calls; keep them.  Value
+      // words pair coordinates 2i (low half) and 2i + 1 (high half).
+      const uint32_t keep16 = (1u << (lo - pg * P)) - 1u;
+      const uint32_t keep = keep16 | (keep16 << 16);
+      uint32_t* words = reinterpret_cast<uint32_t*>(vb);
       for (int p = 0; p < bv; ++p) {
-        uint16_t* plane = reinterpret_cast<uint16_t*>(vb + size_t(p) * plane_bytes);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int c = r * 64 + lane;
-          const uint32_t old = keep ? plane[c] : 0u;
-          plane[c] = uint16_t((old & keep) | vmask[p][r]);
+          const uint32_t mine = vmask[p][r];
+          const uint32_t other = __shfl_xor(mine, 1);
+          if (!(lane & 1)) {
+            const int c = r * 64 + lane;
+            uint32_t* w = words + (c / 2) * bv + p;
+            const uint32_t old = keep ? *w : 0u;
+            *w = (old & keep) | mine | (other << 16);
+          }
         }
       }
     }

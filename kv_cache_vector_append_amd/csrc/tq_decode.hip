@@ -139,14 +139,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         if (page_ok) {
           const uint8_t* kb = cv.k_pages + (size_t(phys) * H + h) * cv.key_block;
           const int t = pos % P;
+          const uint32_t* row = reinterpret_cast<const uint32_t*>(kb) + size_t(t) * (D / 32) * (mk + 1);
           for (int p = 0; p <= mk; ++p) {
-            const uint32_t* row = reinterpret_cast<const uint32_t*>(kb + size_t(p) * plane_bytes + size_t(t) * (D / 8));
 #pragma unroll
-            for (int wi = 0; wi < D / 32; ++wi) words[p][wi] = row[wi];
+            for (int wi = 0; wi < D / 32; ++wi) words[p][wi] = row[wi * (mk + 1) + p];
           }
-          const float* norms = reinterpret_cast<const float*>(kb + size_t(mk + 1) * plane_bytes);
-          knu = norms[t];
-          kgam = norms[P + t];
+          const float* norms = reinterpret_cast<const float*>(kb + size_t(mk + 1) * plane_bytes) + 2 * t;
+          knu = norms[0];
+          kgam = norms[1];
           if (wv == 0) {
             const uint8_t* vb = cv.v_pages + (size_t(phys) * H + h) * cv.value_block;
             vnu_tile[j] = reinterpret_cast<const float*>(vb + size_t(bv) * plane_bytes)[t];
@@ -214,7 +214,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         if (phys < 0 || phys >= cv.num_pages) continue;
         const uint8_t* vb = cv.v_pages + (size_t(phys) * H + h) * cv.value_block;
         uint32_t masks[4];
-        for (int p = 0; p < bv; ++p) masks[p] = reinterpret_cast<const uint16_t*>(vb + size_t(p) * plane_bytes)[c_own];
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vb) + (c_own / 2) * bv;
+        for (int p = 0; p < bv; ++p) masks[p] = (vw[p] >> (16 * (c_own & 1))) & 0xffffu;
         const int nt = min(P, ntok - pgs);
         for (int t = 0; t < nt; ++t) {
           int idx = 0;

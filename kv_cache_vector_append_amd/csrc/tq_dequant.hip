@@ -74,14 +74,14 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int c = r * 64 + lane;
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb) + (size_t(t) * (D / 32) + c / 32) * (mk + 1);
     int idx = 0;
-    for (int p = 0; p < mk; ++p) idx |= int((kb[size_t(p) * plane_bytes + size_t(t) * (D / 8) + c / 8] >> (c % 8)) & 1) << p;
+    for (int p = 0; p < mk; ++p) idx |= int((kw[p] >> (c % 32)) & 1u) << p;
     yr[r] = kc[idx];
-    const int z = (kb[size_t(mk) * plane_bytes + size_t(t) * (D / 8) + c / 8] >> (c % 8)) & 1;
-    sg[r] = z ? -1.f : 1.f;
+    sg[r] = ((kw[mk] >> (c % 32)) & 1u) ? -1.f : 1.f;
   }
-  const float* knorm = reinterpret_cast<const float*>(kb + size_t(mk + 1) * plane_bytes);
-  const float nu = knorm[t], gamma = knorm[P + t];
+  const float* knorm = reinterpret_cast<const float*>(kb + size_t(mk + 1) * plane_bytes) + 2 * t;
+  const float nu = knorm[0], gamma = knorm[1];
   // S^T s: FWHT variant S^T = D1 H_n D2 H; dense variant G^T
   if (ROT == TQ_ROT_FWHT) {
     fwht_then_sign<D>(sg, a.params, kRoleSketch2, lane, 1.0f);
@@ -101,12 +101,12 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a) {
   for (int r = 0; r < R; ++r) ko[r * 64 + lane] = nu * yr[r];
 
   // ---------------- value
-  const uint16_t* vplanes = reinterpret_cast<const uint16_t*>(vb);
+  const uint32_t* vwords = reinterpret_cast<const uint32_t*>(vb);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int c = r * 64 + lane;
     int idx = 0;
-    for (int p = 0; p < bv; ++p) idx |= int((vplanes[size_t(p) * (plane_bytes / 2) + c] >> t) & 1) << p;
+    for (int p = 0; p < bv; ++p) idx |= int((vwords[(c / 2) * bv + p] >> (16 * (c & 1) + t)) & 1u) << p;
     yr[r] = vc[idx];
   }
   const float vnu = reinterpret_cast<const float*>(vb + size_t(bv) * plane_bytes)[t];

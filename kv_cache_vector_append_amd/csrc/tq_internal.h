@@ -92,7 +92,8 @@ struct DecodeArgs {
   const int32_t* seq_slots;
   const int32_t* ctx_len;
   float* out;
-  float* workspace;   // [num_seqs][H_q][splits][2 + 2d]
+  float* workspace;   // plain path: [num_seqs][H_q][splits][2 + 2d]; matrix-core path: query
+                      // operands (decode_prep_bytes), then [num_seqs][H_q][splits][2 + d]
   float* logits;      // optional [num_seqs][H_q][max_ctx]
   int32_t num_seqs, num_q_heads, q_dtype, key_mse_bits, value_bits;
   int32_t splits, split_tokens, max_ctx;
@@ -121,6 +122,7 @@ void build_params(const tq_config& cfg, uint8_t* blob);
 int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream);
 int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
+size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-operand region at the workspace start
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);
 

@@ -81,7 +81,10 @@ def test_size_queries_match_layout():
         assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(d, vb)
         assert tqa.params_bytes(cfg) == 2048 + (3 * d * d * 4 if rot == "dense" else 0)
         ws = tqa.decode_workspace_bytes(cfg, 3, 1000)
-        assert ws > 0 and ws % (4 * (2 + 2 * d)) == 0
+        # at least one partial record (max, denominator, d sums) per (sequence, query head)
+        # for the compressed part and one for the window, in float32
+        assert ws % 4 == 0 and ws >= 2 * 3 * 8 * (2 + d) * 4
+        assert tqa.decode_workspace_bytes(cfg, 3, 100000) > ws
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(key_bits=5), dict(value_bits=0), dict(page_tokens=32),

@@ -243,16 +243,23 @@ def test_layout_bit_positions_by_hand():
     d, m = 128, 2
     codes = np.zeros((16, d), int)
     z = np.zeros((16, d), bool)
-    codes[3, 37] = 2          # plane 1, token 3, coordinate 37
-    z[5, 100] = True          # QJL plane, token 5, coordinate 100
+    codes[3, 37] = 2          # plane 1, token 3, coordinate 37 = group 1 bit 5
+    z[5, 100] = True          # QJL plane (2), token 5, coordinate 100 = group 3 bit 4
     buf = layout.pack_key_block(codes, z, np.zeros(16), np.zeros(16), m)
-    plane = 16 * d // 8
-    nz = np.flatnonzero(buf)
-    assert list(nz) == [plane + 3 * 16 + 37 // 8, 2 * plane + 5 * 16 + 100 // 8]
-    assert buf[plane + 3 * 16 + 4] == 1 << (37 % 8)
+    words_per_token = (d // 32) * (m + 1)
+    w1 = 3 * words_per_token + 1 * (m + 1) + 1
+    w2 = 5 * words_per_token + 3 * (m + 1) + 2
+    assert list(np.flatnonzero(buf)) == [4 * w1, 4 * w2]
+    assert buf[4 * w1] == 1 << 5 and buf[4 * w2] == 1 << 4
+    nu = np.arange(16, dtype=np.float32)
+    gam = -np.arange(16, dtype=np.float32)
+    buf = layout.pack_key_block(codes, z, nu, gam, m)
+    pairs = buf[16 * words_per_token * 4:].view("<f4").reshape(16, 2)
+    assert np.array_equal(pairs[:, 0], nu) and np.array_equal(pairs[:, 1], gam)
     vcodes = np.zeros((16, d), int)
-    vcodes[9, 70] = 3         # both planes, slot 9, coordinate 70
+    vcodes[9, 70] = 3         # both planes, slot 9, coordinate 70 = low half of pair 35
+    vcodes[2, 71] = 1         # plane 0, slot 2, coordinate 71 = high half of pair 35
     vbuf = layout.pack_value_block(vcodes, np.zeros(16), 2)
-    vplane = d * 2
-    assert list(np.flatnonzero(vbuf)) == [70 * 2 + 1, vplane + 70 * 2 + 1]
-    assert vbuf[70 * 2 + 1] == 1 << (9 - 8)
+    words = vbuf[:d * 2 * 2].view("<u4").reshape(d // 2, 2)
+    assert words[35, 0] == (1 << 9) | (1 << (16 + 2)) and words[35, 1] == 1 << 9
+    assert np.count_nonzero(words) == 2
