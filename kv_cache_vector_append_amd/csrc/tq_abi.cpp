@@ -159,7 +159,7 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
 
 size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t max_ctx) {
   if (check_config(cfg) != TQ_OK || num_seqs <= 0 || max_ctx < 0) return 0;
-  const tqi::SplitPlan p = tqi::plan_splits(cfg->head_dim, num_seqs, cfg->num_kv_heads, max_ctx > 0 ? max_ctx : 1);
+  const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, max_ctx > 0 ? max_ctx : 1);
   const size_t partials =
       size_t(num_seqs) * cfg->num_q_heads * (p.splits + 1) * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
   return tqi::decode_prep_bytes(cfg->head_dim, num_seqs, cfg->num_kv_heads) + partials;
@@ -184,7 +184,7 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
   const size_t need = tq_decode_workspace_bytes(cfg, num_seqs, mc);
   if (workspace_bytes < need)
     return fail(TQ_ERR_CAPACITY, "workspace %zu bytes < %zu required", workspace_bytes, need);
-  const tqi::SplitPlan p = tqi::plan_splits(cfg->head_dim, num_seqs, cfg->num_kv_heads, mc);
+  const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, mc);
   tqi::DecodeArgs a{};
   a.cache = view(cfg, cache);
   a.params = static_cast<const uint8_t*>(params_dev);

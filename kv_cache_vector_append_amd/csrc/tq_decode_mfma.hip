@@ -100,6 +100,14 @@ __device__ __forceinline__ float fp8_range_scale(float max_abs) {
 // fp4 element e of a converted word comes from bit fp4_elem_bit(e); inverse:
 __host__ __device__ constexpr int fp4_bit_elem(int b) { return 8 * (b % 4) + b / 4; }
 
+// Byte offset of row/column r, K index k inside a 2048-byte lane-major image of
+// an fp8 operand: bytes 0..15 of every lane first (lane = 16 g + r, 16 bytes
+// each), then bytes 16..31, so each half loads as one conflict-free 16-byte
+// read per lane.
+__host__ __device__ constexpr int fp8_image_offset(int r, int k) {
+  return (k < 64 ? 0 : 1024) + (16 * ((k % 64) / 16) + r) * 16 + (k % 16);
+}
+
 // N consecutive dwords from global memory (N-dword aligned), zeros when !ok
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint32_t* p, bool ok, uint32_t* out) {
@@ -185,89 +193,218 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
-  // per-head power-of-two scales bringing the largest operand entry into (128, 256]
+  // Per head: power-of-two scales bringing the largest operand entry into
+  // (128, 256], and the constants of the affine fp4 encoding of the key bits
+  // (coordinate c falls in element group c % 4): the sums of the scaled
+  // operands over the coordinates with c % 4 < 3.  Tail floats: [0, 4) inverse
+  // key-plane scales, [4, 8) inverse QJL scales, [8, 12) key-plane constants,
+  // [12, 16) QJL constants.
   if (tid < kMaxG) {
-    float cmax = 0.f;
-    for (int i = 0; i < KP; ++i) cmax = fmaxf(cmax, fabsf(coef_k[odd_subset(MK, i)]));
-    float qm = 0.f, qh = 0.f;
+    float csum = 0.f, cmax = 0.f;
+    for (int i = 0; i < KP; ++i) {
+      csum += coef_k[odd_subset(MK, i)];
+      cmax = fmaxf(cmax, fabsf(coef_k[odd_subset(MK, i)]));
+    }
+    float qm = 0.f, qh = 0.f, sm = 0.f, sh = 0.f;
     for (int c = 0; c < D; ++c) {
-      qm = fmaxf(qm, fabsf(q_rot[tid * D + c]));
-      qh = fmaxf(qh, fabsf(q_sk[tid * D + c]));
+      const float f = fabsf(fp4_affine_factor(c & 3));
+      qm = fmaxf(qm, f * fabsf(q_rot[tid * D + c]));
+      qh = fmaxf(qh, f * fabsf(q_sk[tid * D + c]));
+      if ((c & 3) != 3) {
+        sm += q_rot[tid * D + c];
+        sh += q_sk[tid * D + c];
+      }
     }
     qscale[tid] = fp8_range_scale(qm * cmax);
     qscale[kMaxG + tid] = fp8_range_scale(qh);
-    reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048)[tid] = 1.f / qscale[tid];
-    reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048)[kMaxG + tid] = 1.f / qscale[kMaxG + tid];
+    float* tail = reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048);
+    tail[tid] = 1.f / qscale[tid];
+    tail[kMaxG + tid] = 1.f / qscale[kMaxG + tid];
+    tail[2 * kMaxG + tid] = sm * csum * qscale[tid];
+    tail[3 * kMaxG + tid] = sh * qscale[kMaxG + tid];
   }
   __syncthreads();
-  // fp8 parts of a_S * qt (key planes) and of qh (QJL) as operand rows
-  // [plane][half][row = 4 h + part][k].  Coordinate c sits in key word c / 32
+  // fp8 parts of f_j a_S qt (key planes) and of f_j qh (QJL) as lane-major
+  // operand images [plane][half] of rows 4 h + part.  Coordinate c sits in key word c / 32
   // at bit c % 32; word wd feeds half (KH == 2 ? wd & 1 : 0) at K group
   // (KH == 2 ? wd >> 1 : wd), fp4 element fp4_bit_elem(c % 32).
   for (int i = tid; i < (KP + 1) * kMaxG * D; i += T) {
     const int pl = i / (kMaxG * D), rem = i % (kMaxG * D), h = rem / D, c = rem % D;
-    const float x = pl < KP ? q_rot[h * D + c] * coef_k[odd_subset(MK, pl)] * qscale[h]
-                            : q_sk[h * D + c] * qscale[kMaxG + h];
+    const float f = fp4_affine_factor(c & 3);
+    const float x = pl < KP ? f * q_rot[h * D + c] * coef_k[odd_subset(MK, pl)] * qscale[h]
+                            : f * q_sk[h * D + c] * qscale[kMaxG + h];
     const uint32_t parts = fp8_split4(x);
     const int wd = c / 32;
     const int hf = KH == 2 ? (wd & 1) : 0;
     const int kg = KH == 2 ? (wd >> 1) : wd;
     const int k = 32 * kg + fp4_bit_elem(c % 32);
-    uint8_t* row0 = dst + size_t((pl * KH + hf) * 16) * 128;
+    uint8_t* img = dst + size_t(pl * KH + hf) * 2048;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) row0[(h * 4 + p) * 128 + k] = uint8_t(parts >> (8 * p));
+    for (int p = 0; p < 4; ++p) img[fp8_image_offset(h * 4 + p, k)] = uint8_t(parts >> (8 * p));
   }
 }
 
-// ---------------------------------------------------------------------------- window split
-// Positions [nc, L) from the fp16 ring: wavefront wv serves heads wv, wv + NW, ...
-// with lanes holding coordinates r * 64 + lane.  Writes (max, denominator,
-// sum_w p_w v_w) in the value's own (unrotated) basis.
-template <int D, int NW>
-__device__ void window_split(const DecodeArgs& a, float* ws, int s, int hk, int G, int slot, int nc, int L) {
-  constexpr int R = D / 64;
-  __shared__ float wsc[kMaxG][1024];
+// ---------------------------------------------------------------------------- recent-token window
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Positions [nc, L) from the fp16 ring, exactly, on one wavefront, with an
+// online softmax over blocks of 16 tokens; writes (max, denominator,
+// sum_t p_t v_t) per query head in the value's own (unrotated) basis.
+//   scores: v_mfma_f32_16x16x32_f16 with rows 2h + part holding the query of
+//     head h as two fp16 parts (hi + lo, after a power-of-two scale) and
+//     columns the ring's fp16 keys of 16 tokens, so every product is exact and
+//     sums carry fp32 precision;
+//   values: lanes over coordinates, the block's weights broadcast through
+//     `pbuf` (64 floats of LDS).
+// Both score operands place coordinate 32 kc + 8 g + e at element e of lane
+// group g of chunk kc, which pairs the same coordinate on both sides whatever
+// the instruction's internal K order.  A block's ring rows are requested one
+// block ahead.
+template <int D>
+__device__ void window_part(const DecodeArgs& a, float* ws, int s, int hk, int G, int slot, int nc, int L,
+                            float* pbuf) {
+  constexpr int KC = D / 32, NP = D / 128;
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads, W = cv.window;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int nw = L - nc;
   const int rec = 2 + D, nrec = a.splits + 1;
-  const uint16_t* kwin = cv.k_window + (size_t(slot) * H + hk) * W * D;
-  const uint16_t* vwin = cv.v_window + (size_t(slot) * H + hk) * W * D;
-  for (int g = wv; g < G; g += NW) {
-    float q[R];
+  const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
+  float m[kMaxG], l[kMaxG], acc[kMaxG][2 * NP];
 #pragma unroll
-    for (int r = 0; r < R; ++r) q[r] = load_elem(a.q, a.q_dtype, (size_t(s) * a.num_q_heads + hk * G + g) * D + r * 64 + lane);
-    float m = -INFINITY;
-    for (int t = 0; t < nw; ++t) {
-      const uint16_t* kr = kwin + size_t((nc + t) % W) * D;
-      float dot = 0.f;
+  for (int h = 0; h < kMaxG; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) dot = fmaf(q[r], f16_bits_to_float(kr[r * 64 + lane]), dot);
-      dot = wave_sum(dot) * a.scale;
-      if (lane == 0) {
-        wsc[g][t] = dot;
-        if (a.logits) a.logits[(size_t(s) * a.num_q_heads + hk * G + g) * a.max_ctx + nc + t] = dot;
+    for (int j = 0; j < 2 * NP; ++j) acc[h][j] = 0.f;
+  }
+  if (nw > 0) {
+    const uint16_t* kwin = cv.k_window + (size_t(slot) * H + hk) * W * D;
+    const uint16_t* vwin = cv.v_window + (size_t(slot) * H + hk) * W * D;
+    // query operand: row r16 = 2 h + part
+    const int qh = r16 >> 1, part = r16 & 1;
+    const bool qrow_ok = qh < G;
+    float qv[KC][8];
+    float qmax = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[kc][e] = qrow_ok ? load_elem(a.q, a.q_dtype, (qrow0 + qh) * D + 32 * kc + 8 * g4 + e) : 0.f;
+        qmax = fmaxf(qmax, fabsf(qv[kc][e]));
       }
-      m = fmaxf(m, dot);
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+    // power of two bringing the head's largest entry into [256, 512)
+    float qs = 1.f;
+    if (qmax > 0.f) {
+      int e;
+      frexpf(qmax, &e);
+      qs = ldexpf(1.f, 9 - e);
     }
-    float l = 0.f, acc[R];
+    v8h qa[KC];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    for (int t = 0; t < nw; ++t) {
-      const float p = __expf(wsc[g][t] - m);
-      l += p;
-      const uint16_t* vr = vwin + size_t((nc + t) % W) * D;
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = fmaf(p, f16_bits_to_float(vr[r * 64 + lane]), acc[r]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = qv[kc][e] * qs;
+        const _Float16 hi = _Float16(x);
+        qa[kc][e] = part == 0 ? hi : _Float16(x - float(hi));
+      }
+    // result lane (token r16, group g4 < 2): rows 4 g4 + i = heads 2 g4 + i / 2, parts i % 2
+    const int h0 = 2 * g4;
+    const float sc0 = a.scale / __shfl(qs, 2 * h0 & 15);  // rows 2 h hold head h's scale
+    const float sc1 = a.scale / __shfl(qs, 2 * (h0 + 1) & 15);
+    const bool ok0 = g4 < 2 && h0 < G, ok1 = g4 < 2 && h0 + 1 < G;
+
+    uint4 kb[KC];
+    uint32_t vv[16][NP];
+    auto load_block = [&](int t0) {
+      const int rs = (nc + min(t0 + r16, nw - 1)) % W;
+      const uint16_t* kr = kwin + size_t(rs) * D + 8 * g4;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kb[kc] = *reinterpret_cast<const uint4*>(kr + 32 * kc);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t* vr = reinterpret_cast<const uint32_t*>(vwin + size_t((nc + min(t0 + u, nw - 1)) % W) * D);
+#pragma unroll
+        for (int c = 0; c < NP; ++c) vv[u][c] = vr[64 * c + lane];
+      }
+    };
+    load_block(0);
+    for (int t0 = 0; t0 < nw; t0 += 16) {
+      v4f sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kc], __builtin_bit_cast(v8h, kb[kc]), sacc, 0, 0, 0);
+      uint32_t vcur[16][NP];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int c = 0; c < NP; ++c) vcur[u][c] = vv[u][c];
+      load_block(min(t0 + 16, nw - 1));  // unconditional; the last one repeats rows already read
+      const int t = t0 + r16;
+      const bool tok = t < nw;
+      const float s0 = ok0 && tok ? (sacc[0] + sacc[1]) * sc0 : -INFINITY;
+      const float s1 = ok1 && tok ? (sacc[2] + sacc[3]) * sc1 : -INFINITY;
+      if (a.logits) {
+        if (ok0 && tok) a.logits[(qrow0 + h0) * a.max_ctx + nc + t] = s0;
+        if (ok1 && tok) a.logits[(qrow0 + h0 + 1) * a.max_ctx + nc + t] = s1;
+      }
+      // block maxima per head (rows 0 and 1 hold heads 0, 1 and 2, 3)
+      const float b0 = max16(s0), b1 = max16(s1);
+      const float bm[kMaxG] = {row_value(b0, 0), row_value(b1, 0), row_value(b0, 1), row_value(b1, 1)};
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        const float mn = fmaxf(m[h], bm[h]);
+        const float r = mn == m[h] ? 1.f : __expf(m[h] - mn);
+        l[h] *= r;
+#pragma unroll
+        for (int j = 0; j < 2 * NP; ++j) acc[h][j] *= r;
+        m[h] = mn;
+      }
+      const float m0 = g4 == 0 ? m[0] : m[2], m1 = g4 == 0 ? m[1] : m[3];
+      const float p0 = s0 == -INFINITY ? 0.f : __expf(s0 - m0);
+      const float p1 = s1 == -INFINITY ? 0.f : __expf(s1 - m1);
+      if (g4 < 2) {
+        pbuf[r16 * kMaxG + h0] = p0;
+        pbuf[r16 * kMaxG + h0 + 1] = p1;
+      }
+      const float q0 = sum16(p0), q1 = sum16(p1);
+      l[0] += row_value(q0, 0);
+      l[1] += row_value(q1, 0);
+      l[2] += row_value(q0, 1);
+      l[3] += row_value(q1, 1);
+      lds_fence();
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float4 p = *reinterpret_cast<const float4*>(pbuf + u * kMaxG);
+        const float ph[kMaxG] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int c = 0; c < NP; ++c) {
+          const float v0 = f16_bits_to_float(uint16_t(vcur[u][c] & 0xffffu));
+          const float v1 = f16_bits_to_float(uint16_t(vcur[u][c] >> 16));
+#pragma unroll
+          for (int h = 0; h < kMaxG; ++h) {
+            acc[h][2 * c] = fmaf(ph[h], v0, acc[h][2 * c]);
+            acc[h][2 * c + 1] = fmaf(ph[h], v1, acc[h][2 * c + 1]);
+          }
+        }
+      }
+      lds_fence();
     }
-    float* w0 = ws + ((size_t(s) * a.num_q_heads + hk * G + g) * nrec + a.splits) * rec;
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h >= G) break;
+    float* w0 = ws + ((qrow0 + h) * nrec + a.splits) * rec;
     if (lane == 0) {
-      w0[0] = nw > 0 ? m : -INFINITY;
-      w0[1] = l;
+      w0[0] = m[h];
+      w0[1] = l[h];
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) w0[2 + r * 64 + lane] = acc[r];
+    for (int c = 0; c < NP; ++c)
+      *reinterpret_cast<float2*>(w0 + 2 + 128 * c + 2 * lane) = make_float2(acc[h][2 * c], acc[h][2 * c + 1]);
   }
 }
 
@@ -298,8 +435,37 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* out) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int D, int MK, int BV, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
+// Registers per lane a split-kernel variant needs (estimate): value
+// accumulators, query operands unless they sit in LDS, the next block's key
+// words and norms, current and next value words, key-plane staging, and a
+// working margin (scores, addresses) calibrated on the compiled kernels.
+// Two wavefronts per SIMD leave 256.
+constexpr int kRegBudget = 256;
+__host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds) {
+  return num_planes(BV) * (D / 16 / NW) * 4 + (q_in_lds ? 0 : (num_planes(MK) + 1) * (D / 128) * 8) +
+         (8 / NW) * ((MK + 1) * (D / 128) + 3) + 2 * (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + 92;
+}
+__host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
+  return (D / 16) % NW == 0 && 8 % NW == 0 && ((D / 16) / NW) % 2 == 0;
+}
+__host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds) {
+  return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds) <= kRegBudget;
+}
+// wavefronts per work item: the fewest whose registers fit two wavefronts per SIMD
+__host__ __device__ constexpr int split_waves(int D, int MK, int BV) {
+  return split_fits(D, MK, BV, 1, true) ? 1 : split_fits(D, MK, BV, 2, true) ? 2 : split_fits(D, MK, BV, 4, true) ? 4 : 8;
+}
+// query operands stay in registers when they fit, else each MFMA reads them from LDS
+__host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV) {
+  return !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
+}
+
+// Re-base a head's reference maximum only when a block's maximum exceeds it by
+// more than this (weights stay below e^20; fp32 sums keep their range).
+constexpr float kRebase = 20.f;
+
+template <int D, int MK, int BV, int NW, bool QL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
   constexpr int KP = num_planes(MK);   // key plane products
   constexpr int VP = num_planes(BV);   // value plane products
   constexpr int KH = D / 128;          // 128-coordinate halves of the score contraction
@@ -307,14 +473,16 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
   constexpr int CBW = NCB / NW;        // coordinate blocks per wavefront
   constexpr int PPW = 8 / NW;          // pages scored per wavefront per block
   constexpr int KW = (MK + 1) * KH;    // key words per lane per page
-  constexpr int VW = (CBW / 2) * BV;   // value words per lane per page
+  constexpr int VW = (CBW / 2) * BV;   // value words per lane per page pair
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t w_parts[16 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
+  __shared__ __attribute__((aligned(16))) uint8_t q_img[QL ? (KP + 1) * KH * 2048 : 16];  // query operands
   __shared__ float red[NW][8];
   __shared__ float fin[NW][kMaxG];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wvu = NW > 1 ? uniform(wv) : 0;  // wavefront index as a scalar
   const int r16 = lane & 15, g4 = lane >> 4;
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads;
@@ -334,49 +502,60 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
   const int nc = W > 0 ? max(0, L - W) : L;
   const int rec = 2 + D, nrec = a.splits + 1;
   float* ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + part_offset);
-  if (split == a.splits) {
-    // the recent-token window, exactly: fp16 keys and values from the ring
-    window_split<D, NW>(a, ws, s, hk, G, slot, nc, L);
-    return;
-  }
   const int t_begin = split * a.split_tokens;
   const int t_end = min(nc, t_begin + a.split_tokens);
 
-  // query operands of this (sequence, kv head): lane (row r16, group g4)
+  // query operands of this (sequence, kv head), lane-major images
   const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK);
-  v8i qa[KP + 1][KH];
+  v8i qa[QL ? 1 : KP + 1][QL ? 1 : KH];
+  if constexpr (QL) {
+    for (int i = tid; i < (KP + 1) * KH * 128; i += 64 * NW)
+      reinterpret_cast<uint4*>(q_img)[i] = reinterpret_cast<const uint4*>(qp)[i];
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int pl = 0; pl <= KP; ++pl)
+    for (int pl = 0; pl <= KP; ++pl)
 #pragma unroll
-    for (int hf = 0; hf < KH; ++hf) {
-      const uint8_t* src = qp + size_t((pl * KH + hf) * 16 + r16) * 128;
-      const uint4 lo = *reinterpret_cast<const uint4*>(src + 16 * g4);
-      const uint4 hi = *reinterpret_cast<const uint4*>(src + 64 + 16 * g4);
-      qa[pl][hf] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      for (int hf = 0; hf < KH; ++hf) {
+        const uint8_t* img = qp + (pl * KH + hf) * 2048;
+        const uint4 lo = reinterpret_cast<const uint4*>(img)[lane];
+        const uint4 hi = reinterpret_cast<const uint4*>(img + 1024)[lane];
+        qa[pl][hf] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+  }
+  auto qop = [&](int pl, int hf) -> v8i {
+    if constexpr (QL) {
+      const uint8_t* img = q_img + (pl * KH + hf) * 2048;
+      const uint4 lo = reinterpret_cast<const uint4*>(img)[lane];
+      const uint4 hi = reinterpret_cast<const uint4*>(img + 1024)[lane];
+      return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    } else {
+      return qa[pl][hf];
     }
-  const float* qinv = reinterpret_cast<const float*>(qp + (KP + 1) * KH * 2048);
+  };
+  const float* tail = reinterpret_cast<const float*>(qp + (KP + 1) * KH * 2048);
   const bool head_ok = g4 < G;
-  const float inv_sm = qinv[g4], inv_sq = qinv[kMaxG + g4];
+  const float inv_sm = tail[g4], inv_sq = tail[kMaxG + g4];
+  const float k_m = tail[2 * kMaxG + g4], k_q = tail[3 * kMaxG + g4];
   const float qjl_c = kQjlConst / float(D);
 
-  // page addressing: uniform page base + constant per-lane offsets
+  // page addressing: uniform page base + constant per-lane offsets.  Page ids
+  // come through the scalar data cache (uniform addresses in the constant
+  // address space), so waiting for them never waits for page data in flight.
   const uint8_t* kbase = cv.k_pages + size_t(hk) * cv.key_block;
   const uint8_t* vbase = cv.v_pages + size_t(hk) * cv.value_block;
   const size_t kstride = size_t(H) * cv.key_block, vstride = size_t(H) * cv.value_block;
   const uint32_t k_off = uint32_t((r16 * (D / 32) + KH * g4) * (MK + 1) * 4);
   const uint32_t kn_off = uint32_t(kcode_bytes + 8 * r16);
   const uint32_t vn_off = uint32_t(vcode_bytes + 4 * r16);
-  const uint32_t v_off = uint32_t(((NCB * r16 + CBW * wv) / 2) * BV * 4);
-  const int* bt = cv.block_table + size_t(slot) * cv.max_pages_per_seq;
-  auto page_id = [&](int pos0) {  // uniform physical page of the page starting at pos0 (0 if outside)
-    int ph = pos0 < t_end ? bt[pos0 / kPage] : 0;
-    ph = (ph >= 0 && ph < cv.num_pages) ? ph : 0;
-    return uniform(ph);
-  };
-  auto page_ok = [&](int pos0) {
-    if (pos0 >= t_end) return false;
-    const int ph = bt[pos0 / kPage];
-    return ph >= 0 && ph < cv.num_pages;
+  const uint32_t v_off = uint32_t(((NCB * r16 + CBW * wvu) / 2) * BV * 4);
+  typedef const int __attribute__((address_space(4))) const_int;
+  const const_int* bt = (const const_int*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
+  const int last_page = t_end > 0 ? (t_end - 1) / kPage : 0;
+  // physical page of the page starting at pos0, -1 outside [t_begin, t_end) or when invalid
+  auto page_id = [&](int pos0) {
+    const int ph = bt[min(pos0 / kPage, last_page)];
+    return (pos0 < t_end && ph >= 0 && ph < cv.num_pages) ? ph : -1;
   };
 
   v4f acc[VP][CBW];
@@ -384,19 +563,21 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
   for (int p = 0; p < VP; ++p)
 #pragma unroll
     for (int c = 0; c < CBW; ++c) acc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running maximum of head g4 (score layout)
-  float l_part = 0.f;       // this lane's share of head g4's denominator, relative to m_run
-  float sig_run = 0.f;      // power-of-two factor carried by the accumulators (0 = none yet)
+  float m_ref = -INFINITY;  // reference maximum of head g4 (score layout)
+  float l_part = 0.f;       // this lane's share of head g4's denominator, relative to m_ref
 
+  int kid[PPW];  // page ids of the scored pages of the block being loaded
   uint32_t kw[PPW][KW];
   float2 kn[PPW];
   float vn[PPW];
-  uint32_t vw[2][VW];
+  uint32_t vw[2][VW];  // value words of the block
   auto load_keys = [&](int tb) {
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      const uint8_t* kb = kbase + size_t(page_id(tb + (wv * PPW + j) * kPage)) * kstride;
-      const uint8_t* vb = vbase + size_t(page_id(tb + (wv * PPW + j) * kPage)) * vstride;
+      kid[j] = page_id(tb + (wvu * PPW + j) * kPage);
+      const int ph = max(kid[j], 0);
+      const uint8_t* kb = kbase + size_t(ph) * kstride;
+      const uint8_t* vb = vbase + size_t(ph) * vstride;
       load_words<KW>(kb + k_off, kw[j]);
       kn[j] = *reinterpret_cast<const float2*>(kb + kn_off);
       vn[j] = *reinterpret_cast<const float*>(vb + vn_off);
@@ -404,12 +585,16 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
   };
   auto load_values = [&](int tb) {
     // lane group g4 reads pages 2 g4 and 2 g4 + 1 of the block
-    int ph[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ph[j] = page_id(tb + j * kPage);
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
-      const int mine = g4 == 0 ? ph[hp] : g4 == 1 ? ph[2 + hp] : g4 == 2 ? ph[4 + hp] : ph[6 + hp];
+      const int p0 = max(page_id(tb + hp * kPage), 0);
+      const int p1 = max(page_id(tb + (2 + hp) * kPage), 0);
+      const int p2 = max(page_id(tb + (4 + hp) * kPage), 0);
+      const int p3 = max(page_id(tb + (6 + hp) * kPage), 0);
+      int mine = p0;
+      mine = g4 == 1 ? p1 : mine;
+      mine = g4 == 2 ? p2 : mine;
+      mine = g4 == 3 ? p3 : mine;
       load_words<VW>(vbase + size_t(mine) * vstride + v_off, vw[hp]);
     }
   };
@@ -418,10 +603,20 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
     load_keys(t_begin);
     load_values(t_begin);
   }
+  // wait here once for everything requested so far, so that the loop's own
+  // waits only ever cover loads issued inside the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Blocks of 128 tokens.  A block's key words and norms are requested as soon
+  // as the previous block's scores are done, its value words as soon as the
+  // previous block's value tiles are; the requests are unconditional (past
+  // the split's end they fall on page 0 and are not used), so that no wait
+  // depends on a branch.
   for (int tb = t_begin; tb < t_end; tb += kBlock) {
-    const bool more = tb + kBlock < t_end;
     // ---------------------------------------------- scores of this wavefront's pages
     float sc[PPW], vnu[PPW];
+    bool kok[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) kok[j] = kid[j] >= 0;
     float loc_max = -INFINITY, loc_vmax = 0.f;
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
@@ -430,22 +625,15 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
       for (int hf = 0; hf < KH; ++hf) {
         const uint32_t* w = kw[j] + hf * (MK + 1);
 #pragma unroll
-        for (int pl = 0; pl < KP; ++pl) {
-          v8i bop = {0, 0, 0, 0, 0, 0, 0, 0};
-          bits_to_fp4_pm1(plane_word<MK>(w, pl), bop);
-          dm = mfma_f8_f4(qa[pl][hf], bop, dm);
-        }
-        v8i bq = {0, 0, 0, 0, 0, 0, 0, 0};
-        bits_to_fp4_pm1(w[MK], bq);
-        dq = mfma_f8_f4(qa[KP][hf], bq, dq);
+        for (int pl = 0; pl < KP; ++pl) dm = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm);
+        dq = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq);
       }
-      const int pos0 = tb + (wv * PPW + j) * kPage;
-      const int pos = pos0 + r16;
+      const int pos = tb + (wvu * PPW + j) * kPage + r16;
       // dm[i], dq[i]: part i of head g4 for token r16
-      const float msum = fmaf(fmaf(fmaf(dm[3], 0.0625f, dm[2]), 0.0625f, dm[1]), 0.0625f, dm[0]);
-      const float qsum = fmaf(fmaf(fmaf(dq[3], 0.0625f, dq[2]), 0.0625f, dq[1]), 0.0625f, dq[0]);
+      const float msum = fmaf(fmaf(fmaf(dm[3], 0.0625f, dm[2]), 0.0625f, dm[1]), 0.0625f, dm[0]) + k_m;
+      const float qsum = fmaf(fmaf(fmaf(dq[3], 0.0625f, dq[2]), 0.0625f, dq[1]), 0.0625f, dq[0]) + k_q;
       const float est = kn[j].x * fmaf(kn[j].y * qjl_c, qsum * inv_sq, msum * inv_sm);
-      const bool tok_ok = pos < t_end && page_ok(pos0);
+      const bool tok_ok = pos < t_end && kok[j];
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? a.scale * est : -INFINITY;
       vnu[j] = tok_ok ? vn[j] : 0.f;
@@ -453,7 +641,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
     }
-    if (more) load_keys(tb + kBlock);
+    load_keys(tb + kBlock);
     // ---------------------------------------------- block maximum, weight range
     loc_max = max16(loc_max);
     loc_vmax = max16(loc_vmax);
@@ -470,39 +658,47 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
         blk_vmax = fmaxf(blk_vmax, red[w2][4]);
       }
     }
-    const float m_new = fmaxf(m_run, blk_max);
-    const float sig_blk = fp8_range_scale(blk_vmax);
-    const float sig_new = sig_run > 0.f ? fminf(sig_run, sig_blk) : sig_blk;
-    if (m_new != m_run) l_part *= (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
-#pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const float p = (m_new == -INFINITY) ? 0.f : __expf(sc[j] - m_new);
-      l_part += p;
-      const uint32_t parts = fp8_split4(p * vnu[j] * sig_new);
-      const int t = (wv * PPW + j) * kPage + r16;
-      const int k = 32 * (t / 32) + fp4_bit_elem(t % 32);
-#pragma unroll
-      for (int p4 = 0; p4 < 4; ++p4) w_parts[(g4 * 4 + p4) * 128 + k] = uint8_t(parts >> (8 * p4));
-    }
-    // accumulator rescale, only when some head's maximum or the range moved
-    // (value layout: column r16 = (head r16 / 4, part r16 % 4))
-    if (__any((m_new != m_run) || (sig_new != sig_run && sig_run > 0.f))) {
-      const float mo = row_value(m_run, r16 >> 2), mn = row_value(m_new, r16 >> 2);
-      float alpha = (mn == -INFINITY || mo == mn) ? 1.f : __expf(mo - mn);
-      if (sig_run > 0.f) alpha *= sig_new / sig_run;
+    // re-base the reference maximum (rare): weights stay below e^kRebase
+    const bool rebase = blk_max > m_ref + kRebase || (m_ref == -INFINITY && blk_max > -INFINITY);
+    if (__any(rebase)) {
+      const float m_new = rebase ? blk_max : m_ref;
+      const float r = m_new == m_ref ? 1.f : __expf(m_ref - m_new);
+      l_part *= r;
+      // value layout: column r16 = (head r16 / 4, part r16 % 4)
+      const float rv = row_value(r, r16 >> 2);
 #pragma unroll
       for (int p = 0; p < VP; ++p)
 #pragma unroll
-        for (int c = 0; c < CBW; ++c) acc[p][c] *= alpha;
+        for (int c = 0; c < CBW; ++c) acc[p][c] *= rv;
+      m_ref = m_new;
     }
-    m_run = m_new;
-    sig_run = sig_new;
+    // power of two bringing the block's largest weight into (128, 256] as fp8;
+    // the value MFMAs undo it through their E8M0 operand scale
+    const float hd = blk_max - m_ref;  // <= kRebase, -inf for heads without tokens
+    const float hmax = fmaxf(fmaxf(row_value(hd, 0), row_value(hd, 1)), fmaxf(row_value(hd, 2), row_value(hd, 3)));
+    const float bound = blk_vmax * __expf(hmax);
+    int e8 = 0;
+    if (bound > 0.f) {
+      frexpf(bound, &e8);
+      e8 = min(max(8 - e8, -120), 120);
+    }
+    const float wscale = ldexpf(1.f, e8);
+    const int scale_b = kScaleOne - e8;
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const float p = sc[j] == -INFINITY ? 0.f : __expf(sc[j] - m_ref);
+      l_part += p;
+      const uint32_t parts = fp8_split4(p * vnu[j] * wscale);
+      const int t = (wvu * PPW + j) * kPage + r16;
+      const int k = 32 * (t / 32) + fp4_bit_elem(t % 32);
+#pragma unroll
+      for (int p4 = 0; p4 < 4; ++p4) w_img[fp8_image_offset(g4 * 4 + p4, k)] = uint8_t(parts >> (8 * p4));
+    }
     block_sync<NW>();
     // ---------------------------------------------- value tiles of this wavefront
     {
-      const uint8_t* src = w_parts + r16 * 128;
-      const uint4 lo = *reinterpret_cast<const uint4*>(src + 16 * g4);
-      const uint4 hi = *reinterpret_cast<const uint4*>(src + 64 + 16 * g4);
+      const uint4 lo = reinterpret_cast<const uint4*>(w_img)[lane];
+      const uint4 hi = reinterpret_cast<const uint4*>(w_img + 1024)[lane];
       const v8i wop = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
       // operand row r16 of coordinate block CBW wv + c is coordinate NCB r16 + CBW wv + c
 #pragma unroll
@@ -516,15 +712,12 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
         }
 #pragma unroll
         for (int p = 0; p < VP; ++p) {
-          v8i ae = {0, 0, 0, 0, 0, 0, 0, 0}, ao = {0, 0, 0, 0, 0, 0, 0, 0};
-          bits_to_fp4_pm1(plane_word<BV>(we, p), ae);
-          bits_to_fp4_pm1(plane_word<BV>(wo, p), ao);
-          acc[p][2 * cp] = mfma_f4_f8(ae, wop, acc[p][2 * cp]);
-          acc[p][2 * cp + 1] = mfma_f4_f8(ao, wop, acc[p][2 * cp + 1]);
+          acc[p][2 * cp] = mfma_f4_f8(bits_to_fp4_pm1(plane_word<BV>(we, p)), wop, acc[p][2 * cp], scale_b);
+          acc[p][2 * cp + 1] = mfma_f4_f8(bits_to_fp4_pm1(plane_word<BV>(wo, p)), wop, acc[p][2 * cp + 1], scale_b);
         }
       }
     }
-    if (more) load_values(tb + kBlock);
+    load_values(tb + kBlock);
     block_sync<NW>();
   }
 
@@ -541,13 +734,12 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
   }
   if (wv == 0 && r16 == 0 && head_ok) {
     float* w0 = ws + ((size_t(s) * a.num_q_heads + hk * G + g4) * nrec + split) * rec;
-    w0[0] = m_run;
+    w0[0] = m_ref;
     w0[1] = l;
   }
   // values: planes combine in-lane, parts across the lane quad (columns 4h..4h+3)
   const int ch = r16 >> 2, cq = r16 & 3;
   const float part_w = cq == 0 ? 1.f : cq == 1 ? 0.0625f : cq == 2 ? 0.00390625f : 0.000244140625f;
-  const float inv_sig = sig_run > 0.f ? 1.f / sig_run : 0.f;
   float* wsh = ws + ((size_t(s) * a.num_q_heads + hk * G + ch) * nrec + split) * rec + 2;
   float cvals[VP];
 #pragma unroll
@@ -563,40 +755,80 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_split_kernel(DecodeArgs a, 
       v += dpp<0xB1>(v);
       v += dpp<0x4E>(v);
       const int coord = NCB * (4 * g4 + i) + CBW * wv + c;
-      if (cq == 0 && ch < G) wsh[coord] = v * inv_sig;
+      if (cq == 0 && ch < G) wsh[coord] = v;
     }
+  // the recent-token window, exactly, from the fp16 ring: the last split's
+  // first wavefront, in the weight operand's LDS (free after the last block)
+  if (split == a.splits - 1 && wv == 0) window_part<D>(a, ws, s, hk, G, slot, nc, L, reinterpret_cast<float*>(w_img));
 }
 
 // Merge the compressed splits of one (sequence, query head) by log-sum-exp,
 // rotate their value sum back once, add the window's (already unrotated) sum,
-// normalise and store.
+// normalise and store.  The splits' records are read in parallel: maxima and
+// denominators across threads, value sums per coordinate with several loads
+// in flight.
 template <int D, int ROT>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
+  constexpr int NWV = D / 64;
   __shared__ float buf[D];
-  const int c = threadIdx.x;
+  __shared__ float fsp[kMaxSplits + 1];  // split maxima, then their weights
+  __shared__ float red[2][NWV];
+  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   const size_t row = blockIdx.x;  // s * H_q + h
+  const int s = int(row / a.num_q_heads);
   const int rec = 2 + D, nrec = a.splits + 1;
   const float* ws = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.workspace) + part_offset) +
                     row * nrec * rec;
-  float Mc = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) Mc = fmaxf(Mc, ws[sp * rec]);
-  const float Mw = ws[a.splits * rec];
-  const float M = fmaxf(Mc, Mw);
-  float l = 0.f, ar = 0.f, aw = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float m = ws[sp * rec];
-      if (m == -INFINITY) continue;
-      const float f = __expf(m - M);
-      l = fmaf(ws[sp * rec + 1], f, l);
-      ar = fmaf(ws[sp * rec + 2 + c], f, ar);
-    }
-    if (Mw != -INFINITY) {
-      const float f = __expf(Mw - M);
-      l = fmaf(ws[a.splits * rec + 1], f, l);
-      aw = ws[a.splits * rec + 2 + c] * f;
-    }
+  // compressed splits that hold tokens of this sequence (the rest are empty)
+  const CacheView& cv = a.cache;
+  const int slot = a.seq_slots[s];
+  int L = a.ctx_len[s];
+  if (slot < 0 || slot >= cv.max_seqs || L < 0) L = 0;
+  L = min(L, min(cv.max_pages_per_seq * kPage, a.max_ctx));
+  const int nc = cv.window > 0 ? max(0, L - cv.window) : L;
+  const int ns = min(a.splits, (nc + a.split_tokens - 1) / a.split_tokens);
+  // maxima: all splits' in parallel
+  float mloc = -INFINITY;
+  for (int sp = c; sp <= ns; sp += D) {
+    const int idx = sp < ns ? sp : a.splits;  // the window's record last
+    const float m = ws[size_t(idx) * rec];
+    fsp[sp] = m;
+    mloc = fmaxf(mloc, m);
   }
+  mloc = wave_max(mloc);
+  if (lane == 0) red[0][wv] = mloc;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[0][w]);
+  // weights and denominator
+  float lloc = 0.f;
+  for (int sp = c; sp <= ns; sp += D) {
+    const int idx = sp < ns ? sp : a.splits;
+    const float m = fsp[sp];
+    const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
+    fsp[sp] = f;
+    if (f != 0.f) lloc = fmaf(f, ws[size_t(idx) * rec + 1], lloc);
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[1][wv] = lloc;
+  __syncthreads();
+  float l = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) l += red[1][w];
+  // value sums: coordinate c over the splits, eight loads in flight
+  float ar = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= ns; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ws[size_t(sp + u) * rec + 2 + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ar = fmaf(fsp[sp + u], v[u], ar);
+  }
+  for (; sp < ns; ++sp) ar = fmaf(fsp[sp], ws[size_t(sp) * rec + 2 + c], ar);
+  const float fw = fsp[ns];
+  const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
   buf[c] = ar;
   __syncthreads();
   float o;
@@ -605,23 +837,26 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, size_t 
     o = apply_sign(buf[c] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c));
   } else {
     const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D;
-    o = 0.f;
-    for (int j = 0; j < D; ++j) o = fmaf(piv[size_t(j) * D + c], buf[j], o);
+    float o4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int j = 0; j < D; j += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o4[u] = fmaf(piv[size_t(j + u) * D + c], buf[j + u], o4[u]);
+    o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
   }
   a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
 }
 
 template <int D, int MK, int BV, int ROT>
 hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
-  // one wavefront per work item unless its value tiles exceed 32 (128 accumulators)
-  constexpr int tiles = num_planes(BV) * (D / 16);
-  constexpr int NW = tiles <= 32 ? 1 : tiles <= 64 ? 2 : 4;
+  constexpr int NW = split_waves(D, MK, BV);
+  constexpr bool QL = split_q_in_lds(D, MK, BV);
   const int H = a.cache.num_kv_heads;
   const size_t part_offset = decode_prep_bytes(D, a.num_seqs, H);
   hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT>), dim3(a.num_seqs * H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW>), dim3(a.num_seqs * H, a.splits + 1), dim3(64 * NW), 0, st,
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW), 0, st,
                      a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -643,6 +878,18 @@ hipError_t dispatch_bits(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int decode_mfma_waves(const tq_config& cfg) {
+  const int d = cfg.head_dim, mk = cfg.key_bits - 1, bv = cfg.value_bits;
+  if (mk < 1 || mk > 3 || bv < 1 || bv > 4 || (d != 128 && d != 256)) return 1;
+  constexpr int w128[3][4] = {{split_waves(128, 1, 1), split_waves(128, 1, 2), split_waves(128, 1, 3), split_waves(128, 1, 4)},
+                              {split_waves(128, 2, 1), split_waves(128, 2, 2), split_waves(128, 2, 3), split_waves(128, 2, 4)},
+                              {split_waves(128, 3, 1), split_waves(128, 3, 2), split_waves(128, 3, 3), split_waves(128, 3, 4)}};
+  constexpr int w256[3][4] = {{split_waves(256, 1, 1), split_waves(256, 1, 2), split_waves(256, 1, 3), split_waves(256, 1, 4)},
+                              {split_waves(256, 2, 1), split_waves(256, 2, 2), split_waves(256, 2, 3), split_waves(256, 2, 4)},
+                              {split_waves(256, 3, 1), split_waves(256, 3, 2), split_waves(256, 3, 3), split_waves(256, 3, 4)}};
+  return d == 128 ? w128[mk - 1][bv - 1] : w256[mk - 1][bv - 1];
+}
 
 size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads) {
   // sized for the largest key bit width, 256-byte aligned

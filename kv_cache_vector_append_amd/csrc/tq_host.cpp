@@ -221,13 +221,19 @@ void write_signs(uint8_t* blob, uint64_t seed, int d) {
 
 }  // namespace
 
-SplitPlan plan_splits(int d, int num_seqs, int num_kv_heads, int max_ctx) {
-  (void)d;
-  const int units = (num_seqs > 0 ? num_seqs : 1) * num_kv_heads;
-  const int tile = 64;
+// Context splits per (sequence, KV head): enough work items to fill the
+// chip's resident wavefront slots (two per SIMD, 1024 SIMDs) and no more, each
+// a whole number of tiles (the matrix-core kernel's 128-token blocks, the
+// plain kernel's 64-token tiles).
+SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
+  const bool mfma = decode_mfma_supported(cfg);
+  const int units = (num_seqs > 0 ? num_seqs : 1) * cfg.num_kv_heads;
+  const int tile = mfma ? 128 : 64;
+  const int items = mfma ? 2048 / decode_mfma_waves(cfg) : 2048;
   const int max_tiles = (max_ctx + tile - 1) / tile;
-  int splits = (2048 + units - 1) / units;
+  int splits = (items + units - 1) / units;
   if (splits > max_tiles) splits = max_tiles;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
   const int per = (max_ctx + splits - 1) / splits;
   int split_tokens = ((per + tile - 1) / tile) * tile;

@@ -113,7 +113,9 @@ struct SplitPlan {
   int splits;
   int split_tokens;
 };
-SplitPlan plan_splits(int d, int num_seqs, int num_kv_heads, int max_ctx);
+// At most kMaxSplits context splits per (sequence, KV head).
+constexpr int kMaxSplits = 2048;
+SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx);
 
 // Host-side parameter construction (tq_host.cpp).
 void build_params(const tq_config& cfg, uint8_t* blob);
@@ -122,6 +124,7 @@ void build_params(const tq_config& cfg, uint8_t* blob);
 int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream);
 int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
+int decode_mfma_waves(const tq_config& cfg);  // wavefronts per (sequence, KV head, split) work item
 size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-operand region at the workspace start
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);

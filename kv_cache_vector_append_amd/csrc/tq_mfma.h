@@ -4,12 +4,16 @@
 // softmax weights x decoded values -- run on v_mfma_scale_f32_16x16x128_f8f6f4
 // with one operand in fp4 (e2m1) and the other in fp8 (e4m3, OCP encoding):
 //
-//  * Every code bit-plane maps to a +-1 fp4 operand: a symmetric Lloyd-Max
-//    codebook is an odd function of the code's sign bits s_k = 1 - 2 bit_k,
+//  * Every code bit-plane is a +-1 matrix: a symmetric Lloyd-Max codebook is
+//    an odd function of the code's sign bits s_k = 1 - 2 bit_k,
 //    c[idx] = sum over odd subsets S of a_S prod_{k in S} s_k, so a dot
 //    product with decoded codes is a weighted sum of +-1 plane products, and
-//    the QJL bits are +-1 already.  Bits turn into fp4 nibbles with two ALU
-//    operations per 8 values.
+//    the QJL bits are +-1 already.  Key bits turn into fp4 operands with one
+//    ALU operation per 8 values through an affine encoding
+//    (bits_to_fp4_affine); value bits, whose products are summed over many
+//    tokens, keep the centred +-1 encoding (bits_to_fp4_pm1): an affine
+//    offset there grows with the token count while the result does not, and
+//    costs accuracy in the matrix-core sums.
 //  * The fp32 operand (rotated query, softmax weight) is split into four fp8
 //    parts x = sum_p 16^-p x_p held in four operand rows; the fp32 accumulator
 //    then carries about 2^-17 relative precision, far below the fp32 -> fp64
@@ -30,6 +34,7 @@
 namespace tqi {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp8 = 0;
@@ -41,19 +46,37 @@ __device__ __forceinline__ v4f mfma_f8_f4(const v8i& a, const v8i& b, v4f acc) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp8, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
 }
 
-// acc += A(fp4) x B(fp8)
-__device__ __forceinline__ v4f mfma_f4_f8(const v8i& a, const v8i& b, v4f acc) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp4, kFmtFp8, 0, kScaleOne, 0, kScaleOne);
+// acc += A(fp4) x B(fp8) * 2^(scale_b - 127)   (scale_b: E8M0 exponent, the same in every lane)
+__device__ __forceinline__ v4f mfma_f4_f8(const v8i& a, const v8i& b, v4f acc, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp4, kFmtFp8, 0, kScaleOne, 0, scale_b);
 }
 
-// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0).  Output dword j, nibble
-// n holds bit 4n + j of w, so fp4 element e = 8j + n comes from bit
-// 4(e % 8) + e / 8.
-__device__ __forceinline__ void bits_to_fp4_pm1(uint32_t w, v8i& out) {
-  out[0] = int(((w << 3) & 0x88888888u) | 0x22222222u);
-  out[1] = int(((w << 2) & 0x88888888u) | 0x22222222u);
-  out[2] = int(((w << 1) & 0x88888888u) | 0x22222222u);
-  out[3] = int((w & 0x88888888u) | 0x22222222u);
+// 32 code bits -> 32 fp4 values, one ALU operation per 8 values.  Dword j
+// takes the bits 4n + j of w (n = 0..7) in place, so fp4 element e = 8j + n
+// comes from bit 4(e % 8) + e / 8, and a set bit reads as 0.5, 1.0 or 2.0 for
+// j = 0, 1, 2 (clear: 0) and as -1.0 for j = 3 (clear: +1.0).  With
+// s = 1 - 2 bit, the +-1 sign of a bit is s = 1 + f_j v for j < 3 and s = v
+// for j = 3, where v is the fp4 value and f_j = -4, -2, -1; so
+//   sum_c x_c s_c = sum_{c : j(c) < 3} x_c + sum_c (f_j(c) x_c) v_c,
+// i.e. the other operand carries the factor f_j and a per-row constant is
+// added to the product.
+__device__ __forceinline__ v8i bits_to_fp4_affine(uint32_t w) {
+  const v4i lo = {int(w & 0x11111111u), int(w & 0x22222222u), int(w & 0x44444444u),
+                  int((w & 0x88888888u) | 0x22222222u)};
+  // an fp4 operand occupies the low four registers; the upper four are not read
+  return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0), same element order.
+__device__ __forceinline__ v8i bits_to_fp4_pm1(uint32_t w) {
+  const v4i lo = {int(((w << 3) & 0x88888888u) | 0x22222222u), int(((w << 2) & 0x88888888u) | 0x22222222u),
+                  int(((w << 1) & 0x88888888u) | 0x22222222u), int((w & 0x88888888u) | 0x22222222u)};
+  return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// Operand factor f_j for the element group j = (bit position) % 4 of the above.
+__host__ __device__ constexpr float fp4_affine_factor(int j) {
+  return j == 0 ? -4.f : j == 1 ? -2.f : j == 2 ? -1.f : 1.f;
 }
 
 // Bit position inside a 32-bit source word of fp4 element e (inverse of the above).
