@@ -83,6 +83,87 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+# Sources each call's kernels are built from (the traffic entry is only used
+# while they are unchanged) and the kernels one call launches.
+_CSRC = "kv_cache_vector_append_amd/csrc/"
+SOURCES = {
+    "decode": [_CSRC + f for f in ("tq_decode_mfma.hip", "tq_mfma.h", "tq_decode.hip", "tq_device.h",
+                                   "tq_internal.h")],
+    "append": [_CSRC + f for f in ("tq_append.hip", "tq_device.h", "tq_internal.h")],
+}
+KERNELS = {
+    "decode": "tq_decode_attention (decode_prep + decode_split + decode_combine)",
+    "append": "tq_quantize_append (append_kernel)",
+}
+# rocprofv3 kernel-name prefixes of each call's kernels
+KERNEL_MATCH = {"decode": ("decode_prep_kernel", "decode_split_kernel", "decode_combine_kernel"),
+                "append": ("append_kernel",)}
+CALIBRATION_BYTES = 1 << 30
+
+
+def calibration_copy():
+    """One plain device-to-device copy of CALIBRATION_BYTES (read once, written
+    once), whose FETCH_SIZE / WRITE_SIZE calibrate the counters' units."""
+    import torch
+    a = torch.zeros(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    # an elementwise kernel with a name nothing else in the run has (a plain
+    # memcpy may run on a DMA engine, which the counters do not see)
+    torch.bitwise_not(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def _counter_sums(path, counter):
+    """Per-dispatch values of `counter` from a rocprofv3 counter_collection.csv:
+    {kernel name: [value per dispatch]}."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def write_traffic(fetch_csv, write_csv, workload):
+    fetch = _counter_sums(fetch_csv, "FETCH_SIZE")
+    write = _counter_sums(write_csv, "WRITE_SIZE")
+
+    def copy_kib(d):
+        # the calibration kernel is the run's only bitwise-not
+        cands = [max(v) for k, v in d.items() if "bitwise_not" in k.lower() or "bitwisenot" in k.lower()]
+        return max(cands) if cands else None
+
+    fk, wk = copy_kib(fetch), copy_kib(write)
+    f_scale = CALIBRATION_BYTES / fk if fk else None   # bytes per counted unit
+    w_scale = CALIBRATION_BYTES / wk if wk else None
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data["_calibration"] = {"copy_bytes": CALIBRATION_BYTES, "fetch_units": fk, "write_units": wk,
+                            "fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale}
+    for call, names in KERNEL_MATCH.items():
+        per_kernel = {}
+        for n in names:
+            fv = [v for k, vals in fetch.items() if n in k for v in vals]
+            wv = [v for k, vals in write.items() if n in k for v in vals]
+            if fv and wv:
+                per_kernel[n] = (float(np.median(fv)), float(np.median(wv)))
+        if len(per_kernel) != len(names) or not f_scale or not w_scale:
+            continue
+        fb = sum(v[0] for v in per_kernel.values()) * f_scale
+        wb = sum(v[1] for v in per_kernel.values()) * w_scale
+        data[f"{call}:{workload}"] = {
+            "hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+            "per_kernel_median_units": per_kernel, "source_hash": source_hash(SOURCES[call])}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(data, indent=1, sort_keys=True))
+    return 0
+
+
 def measured_traffic(kernel_key, src_hash):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
@@ -180,24 +261,40 @@ def build_mixed_setup(w, tqa, torch, dev):
     return S
 
 
-def run_gpu(w, steps, warmup):
+def replicate_cache(S, tqa, w, copies):
+    """Independent copies of the filled cache (pages and fp16 rings), so that
+    consecutive steps never find the previous step's pages in the 256 MB
+    last-level cache."""
+    c = S.cache
+    S.caches = [c] + [tqa.CacheBuffers(c.k_pages.clone(), c.v_pages.clone(), c.block_table,
+                                       None if c.k_window is None else c.k_window.clone(),
+                                       None if c.v_window is None else c.v_window.clone())
+                      for _ in range(copies - 1)]
+
+
+def run_gpu(w, steps, warmup, copies):
     import torch
     import kv_cache_vector_append_amd as tqa
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S = build_mixed_setup(w, tqa, torch, dev) if w.prefill_seqs else build_decode_setup(w, tqa, torch, dev)
+    if copies <= 0:
+        copies = 4 if decode_algorithmic_bytes(w, S.lens) < 2 ** 30 else 1
+    replicate_cache(S, tqa, w, copies)
+    torch.cuda.synchronize()
+    log(f"{copies} cache copies rotated across steps")
     stream = torch.cuda.current_stream()
 
-    def append():
-        tqa.quantize_append(S.cfg, S.params, S.cache, S.step_k, S.step_v, *S.app_args, stream=stream)
+    def append(i):
+        tqa.quantize_append(S.cfg, S.params, S.caches[i % copies], S.step_k, S.step_v, *S.app_args, stream=stream)
 
-    def decode():
-        tqa.decode_attention(S.cfg, S.params, S.cache, S.q, S.dec_slots, S.dec_lens, S.max_ctx, S.out, S.ws,
-                             stream=stream)
+    def decode(i):
+        tqa.decode_attention(S.cfg, S.params, S.caches[i % copies], S.q, S.dec_slots, S.dec_lens, S.max_ctx, S.out,
+                             S.ws, stream=stream)
 
-    for _ in range(warmup):
-        append()
-        decode()
+    for i in range(warmup):
+        append(i)
+        decode(i)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -207,9 +304,9 @@ def run_gpu(w, steps, warmup):
     t0.record(stream)
     for i in range(steps):
         ev[i][0].record(stream)
-        append()
+        append(warmup + i)
         ev[i][1].record(stream)
-        decode()
+        decode(warmup + i)
         ev[i][2].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -222,7 +319,7 @@ def run_gpu(w, steps, warmup):
     log(f"{steps} steps: {total_ms:.3f} ms on the stream ({wall * 1e3:.1f} ms wall); "
         f"append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us per call")
     return dict(total_ms=total_ms, app_ms=app_ms, dec_ms=dec_ms, lens=S.lens, app_counts=S.app_counts,
-                app_lens_after=S.app_lens_after)
+                app_lens_after=S.app_lens_after, copies=copies)
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
@@ -279,25 +376,32 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated across steps (0: 4 when the decode working set is under 1 GiB)")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a bench run "
+                         "with --calibrate-copy into profiles/traffic.json entries, then exit")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy, whose counters calibrate the byte counts")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         return 2
     import workloads
     w = workloads.WORKLOADS[args.workload]
-    r = run_gpu(w, args.steps, args.warmup)
+    if args.calibrate_copy:
+        calibration_copy()
+    r = run_gpu(w, args.steps, args.warmup, args.copies)
     ms = r["total_ms"] / args.steps
     cached = sum(r["lens"])
     value = cached / (ms / 1e3)
     dec_bytes = decode_algorithmic_bytes(w, r["lens"])
     app_bytes = append_algorithmic_bytes(w, r["app_counts"], r["app_lens_after"])
-    calls = {
-        "decode": dict(ms=r["dec_ms"], bytes=dec_bytes,
-                       src=["kv_cache_vector_append_amd/csrc/tq_decode.hip", "kv_cache_vector_append_amd/csrc/tq_device.h"]),
-        "append": dict(ms=r["app_ms"], bytes=app_bytes,
-                       src=["kv_cache_vector_append_amd/csrc/tq_append.hip", "kv_cache_vector_append_amd/csrc/tq_device.h"]),
-    }
+    calls = {"decode": dict(ms=r["dec_ms"], bytes=dec_bytes, src=SOURCES["decode"]),
+             "append": dict(ms=r["app_ms"], bytes=app_bytes, src=SOURCES["append"])}
     dom = max(calls, key=lambda k: calls[k]["ms"])
     c = calls[dom]
     achieved = c["bytes"] / (c["ms"] / 1e3) / 1e9
@@ -305,7 +409,7 @@ def main(argv=None):
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(f"{dom}:{w.name}", src_hash),
-                "kernel": f"tq_{dom} ({'decode_split + decode_combine' if dom == 'decode' else 'append_kernel'})",
+                "kernel": KERNELS[dom],
                 "algorithmic_bytes_per_launch": int(c["bytes"]), "avg_launch_ms": round(c["ms"], 5),
                 "source_hash": src_hash}
     other = [k for k in calls if k != dom][0]
@@ -321,6 +425,7 @@ def main(argv=None):
                    "head_dim": w.head_dim, "key_bits": w.key_bits, "value_bits": w.value_bits,
                    "rotation": w.rotation, "window": w.window, "page_tokens": w.page_tokens},
         "roofline": roofline,
+        "cache_copies": r["copies"],
         f"{other}_call": {"avg_launch_ms": round(oc["ms"], 5), "algorithmic_bytes_per_launch": int(oc["bytes"]),
                           "achieved_GBs": round(oc["bytes"] / (oc["ms"] / 1e3) / 1e9, 2)},
     }
