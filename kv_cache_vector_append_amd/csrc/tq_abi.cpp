@@ -146,13 +146,9 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
   a.dtype = dtype;
   a.key_mse_bits = cfg->key_bits - 1;
   a.value_bits = cfg->value_bits;
-  // one worker per page a sequence's new tokens may touch, capped for huge prefills
-  int parts = (max_new_per_seq + cfg->page_tokens - 1) / cfg->page_tokens + 1;
-  if (parts > 4096) parts = 4096;
-  a.parts = parts;
-  const long long units = (long long)num_seqs * cfg->num_kv_heads * parts;
-  if (units > 0x7fffffffLL) return fail(TQ_ERR_CAPACITY, "append launch too large");
-  const int e = tqi::launch_append(*cfg, a, int(units), stream);
+  if ((long long)num_seqs * cfg->num_kv_heads * ((max_new_per_seq + 15) / 16 + 1) > 0x7fffffffLL)
+    return fail(TQ_ERR_CAPACITY, "append launch too large");
+  const int e = tqi::launch_append(*cfg, a, num_seqs, max_new_per_seq, stream);
   if (e != 0) return hip_fail(e, "append launch");
   return TQ_OK;
 }

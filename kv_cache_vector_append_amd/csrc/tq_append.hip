@@ -10,14 +10,21 @@
 //   pack the bit-planes into page block_table[slot][pos / 16], slot pos % 16,
 //   and copy the last `window` tokens to the fp16 ring.
 //
-// Work decomposition: one 64-lane wavefront per (sequence, kv head, part);
-// the part strides over the pages the sequence's new tokens touch, so a page
-// is only ever written by one wavefront in a call.  Lanes hold coordinates
-// (lane l owns coordinates r*64 + l), so the Walsh-Hadamard butterflies are
-// cross-lane shuffles, the norms are wavefront reductions, and each key
-// bit-plane row is one wavefront ballot.  Value bit-planes are stored per
-// coordinate (16 token bits), which each lane accumulates in registers over
-// the page's tokens and writes once.
+// Two kernels:
+//  * append_tok_kernel (FWHT rotation, d = 64 or 128, appends of 32 or more
+//    tokens per sequence): a lane per token, everything in registers; see the
+//    comment above it.
+//  * append_kernel (the dense rotation, d = 256, and short appends): one
+//    64-lane wavefront per (sequence, kv head, part); the part strides over the
+//    pages the sequence's new tokens touch, so a page is only ever written by
+//    one wavefront in a call.  Lanes hold coordinates (lane l owns coordinates
+//    r*64 + l), so the Walsh-Hadamard butterflies are cross-lane shuffles, the
+//    norms are wavefront reductions, and each key bit-plane row is one
+//    wavefront ballot.  Value bit-planes are stored per coordinate (16 token
+//    bits), which each lane accumulates in registers over the page's tokens and
+//    writes once.
+#include <type_traits>
+
 #include "tq_device.h"
 
 namespace tqi {
@@ -253,6 +260,424 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token-per-lane append (FWHT rotation, d = 64 or 128).
+//
+// One wavefront takes 64 consecutive positions (four pages) of one
+// (sequence, kv head); lane l owns position P0 + l and holds its whole head
+// vector in registers, so the Walsh-Hadamard butterflies, the norms and the
+// code decisions involve no other lane.  Instead of scaling d coordinates by
+// 1 / (sqrt(d) nu), each lane scales its thresholds and centroids by
+// sqrt(d) nu and works on z = H D x directly: y > t  <=>  z > t sqrt(d) nu,
+// and the QJL signs of S e do not change under the positive factor.  Key
+// bit-plane words are built by shifting the comparison bits in; value planes,
+// stored per coordinate with the page's 16 token slots in a word, come from
+// the comparisons' lane masks (one mask = 64 tokens of one coordinate),
+// handed to the lane that stores that coordinate pair.
+typedef const uint32_t __attribute__((address_space(4))) const_u32;
+typedef const int32_t __attribute__((address_space(4))) const_i32;
+typedef const float __attribute__((address_space(4))) const_f32;
+
+template <int N>
+__device__ __forceinline__ void fwht_regs(float (&x)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h)
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// v with lane L replaced by the uniform value s (v_writelane_b32, immediate
+// lane select)
+template <int L>
+__device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t s) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(L));
+  return v;
+}
+
+// Keeps the scheduler from moving work across phases (loads of the next phase
+// hoisted over a long computation would hold its registers throughout).
+__device__ __forceinline__ void phase() { __builtin_amdgcn_sched_barrier(0); }
+
+// x <- D x, with D as a table of +-1.0 in LDS (read as broadcasts)
+template <int N>
+__device__ __forceinline__ void flip_signs(float (&x)[N], const float* sgn) {
+#pragma unroll
+  for (int c = 0; c < N; c += 4) {
+    const float4 s4 = *reinterpret_cast<const float4*>(sgn + c);
+    x[c] *= s4.x;
+    x[c + 1] *= s4.y;
+    x[c + 2] *= s4.z;
+    x[c + 3] *= s4.w;
+    if ((c & 31) == 28) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight
+  }
+}
+
+// Row `row` of a [rows][N] input of the given dtype, as fp32.
+template <int N>
+__device__ __forceinline__ void load_row(const void* src, int dtype, size_t row, float (&x)[N]) {
+  if (dtype == TQ_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + row * N);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 f = p[q];
+      x[4 * q] = f.x; x[4 * q + 1] = f.y; x[4 * q + 2] = f.z; x[4 * q + 3] = f.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + row * N);
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int q = 0; q < N / 8; ++q) {
+      const uint4 u = p[q];
+      w[4 * q] = u.x; w[4 * q + 1] = u.y; w[4 * q + 2] = u.z; w[4 * q + 3] = u.w;
+    }
+    if (dtype == TQ_BF16) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        x[2 * i] = f16_bits_to_float(uint16_t(w[i] & 0xffffu));
+        x[2 * i + 1] = f16_bits_to_float(uint16_t(w[i] >> 16));
+      }
+    }
+  }
+}
+
+// fp16 copy of a row into the ring
+template <int N>
+__device__ __forceinline__ void store_f16_row(uint16_t* dst, const float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 8; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = uint32_t(float_to_f16_bits(x[8 * q + 2 * i])) | (uint32_t(float_to_f16_bits(x[8 * q + 2 * i + 1])) << 16);
+    reinterpret_cast<uint4*>(dst)[q] = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Codes of z for an odd codebook of L = 2^M levels, in sign-bit form.  The
+// host builds the codebook odd (c[L-1-j] = -c[j]), so the fp32 thresholds are
+// odd too and the middle one is 0: idx = #{t_j < z} has top bit [z > 0] and
+// lower bits equal to the magnitude index m = #{tu_k < |z|} over the upper
+// thresholds tu = t[L/2 .. L-2], complemented when z < 0 (up to ties, which
+// sit inside any rounding band).  Every decision is kept as the sign bit of a
+// float: bit j of m is the sign of d_j = tu_(...) - |z| (a binary search), the
+// code's top bit is NOT sign(z), and its bit j < M-1 is sign(d_j XOR z).  Bits
+// are shifted into words with v_alignbit and selections use masks built from
+// sign bits, so no comparison result has to stay alive as a lane mask.
+__device__ __forceinline__ uint32_t sign_mask(float d) { return uint32_t(int32_t(__float_as_uint(d)) >> 31); }
+__device__ __forceinline__ float pick(uint32_t m, float if_set, float if_clear) {
+  return __uint_as_float((__float_as_uint(if_set) & m) | (__float_as_uint(if_clear) & ~m));
+}
+// w <- (w << 1) | sign bit of v
+__device__ __forceinline__ uint32_t shift_in_sign(uint32_t w, uint32_t v) { return __builtin_amdgcn_alignbit(w, v, 31); }
+
+// d[j] for the magnitude bits j = 0 .. M-2 of |z| = a (entries >= M-1 unused)
+template <int M>
+__device__ __forceinline__ void magnitude_signs(float a, const float* tu, float (&d)[4]) {
+  if constexpr (M == 2) {
+    d[0] = tu[0] - a;
+  } else if constexpr (M == 3) {
+    d[1] = tu[1] - a;
+    d[0] = pick(sign_mask(d[1]), tu[2], tu[0]) - a;
+  } else if constexpr (M == 4) {
+    d[2] = tu[3] - a;
+    const uint32_t m2 = sign_mask(d[2]);
+    d[1] = pick(m2, tu[5], tu[1]) - a;
+    const uint32_t m1 = sign_mask(d[1]);
+    d[0] = pick(m2, pick(m1, tu[6], tu[4]), pick(m1, tu[2], tu[0])) - a;
+  }
+}
+
+// |c[idx]| from the magnitude bits (odd codebook: c[idx] = +-cu[m])
+template <int M>
+__device__ __forceinline__ float centroid_mag(const float* cu, const float (&d)[4]) {
+  if constexpr (M == 1) {
+    return cu[0];
+  } else if constexpr (M == 2) {
+    return pick(sign_mask(d[0]), cu[1], cu[0]);
+  } else {
+    const uint32_t m1 = sign_mask(d[1]), m0 = sign_mask(d[0]);
+    return pick(m1, pick(m0, cu[3], cu[2]), pick(m0, cu[1], cu[0]));
+  }
+}
+
+template <int D, int MK, int BV>
+__global__ __launch_bounds__(64) void append_tok_kernel(AppendArgs a) {
+  constexpr int P = 16, NG = D / 32;
+  // upper thresholds and centroids of the odd codebooks (at least one entry)
+  constexpr int NKT = (1 << (MK - 1)) - 1 > 0 ? (1 << (MK - 1)) - 1 : 1, NKC = 1 << (MK - 1);
+  constexpr int NVT = (1 << (BV - 1)) - 1 > 0 ? (1 << (BV - 1)) - 1 : 1;
+  constexpr int KWORDS = NG * (MK + 1);
+  const int lane = threadIdx.x;
+  const CacheView& cv = a.cache;
+  const int H = cv.num_kv_heads, W = cv.window;
+  int unit = blockIdx.x;
+  const int chunk = unit % a.parts;
+  unit /= a.parts;
+  const int h = unit % H;
+  const int s = unit / H;
+  if (s >= a.num_seqs) return;
+  const int slot = a.seq_slots[s];
+  if (slot < 0 || slot >= cv.max_seqs) return;
+  const int start = a.ctx_len_before[s];
+  const int b0 = a.cu_new_tokens[s];
+  const int n = a.cu_new_tokens[s + 1] - b0;
+  if (n <= 0 || start < 0) return;
+  const int new_len = start + n;
+  const int P0 = (start / 64 + chunk) * 64;
+  if (P0 >= new_len) return;
+  const int pos = P0 + lane;
+  const bool valid = pos >= start && pos < new_len;
+  const int g = lane >> 4, t = lane & 15;
+
+  // the four pages of this chunk (uniform ids through the scalar cache)
+  const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
+  int phys[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pg = P0 / P + j;
+    const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
+    phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
+  }
+  int my_phys = phys[0];
+  my_phys = g == 1 ? phys[1] : my_phys;
+  my_phys = g == 2 ? phys[2] : my_phys;
+  my_phys = g == 3 ? phys[3] : my_phys;
+  const bool page_ok = valid && my_phys >= 0;
+  const bool in_window = valid && W > 0 && pos >= new_len - W;
+  const size_t row = (size_t(b0) + (pos - start)) * H + h;
+
+  const const_f32* prm = (const const_f32*)a.params;
+  // the four sign vectors (roles KR, KS1, KS2, VR) as +-1.0 tables
+  __shared__ __attribute__((aligned(16))) float sgn[4][D];
+  {
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(a.params + kOffSigns);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = lane; c < D; c += 64)
+        sgn[r][c] = ((sw[r * (kSignRoleBytes / 4) + (c >> 5)] >> (c & 31)) & 1u) ? -1.f : 1.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const float sqd = sqrtf(float(D));
+  const size_t plane_bytes = size_t(P) * D / 8;
+
+  float x[D];
+  // ------------------------------------------------------------------ key
+  if (valid) {
+    load_row<D>(a.k_new, a.dtype, row, x);
+  } else {
+#pragma unroll
+    for (int c = 0; c < D; ++c) x[c] = 0.f;
+  }
+  if (in_window) store_f16_row<D>(cv.k_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
+  const float nu = sqrtf(ss);
+  const bool zero = !(nu >= kZeroNorm);
+  const float kscale = zero ? 0.f : sqd * nu;
+  float tk[NKT], ck[NKC];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kscale;
+#pragma unroll
+  for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kscale;
+  phase();
+  flip_signs<D>(x, sgn[kRoleKeyRot]);
+  fwht_regs<D>(x);
+  phase();
+  // codes, residual e = z - c[idx] (in place), its norm
+  uint32_t kw[MK + 1][NG];
+  float es = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+    for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
+#pragma unroll
+    for (int k = 31; k >= 0; --k) {
+      const int c = 32 * gg + k;
+      const float z = x[c];
+      const uint32_t zb = __float_as_uint(z);
+      float dm[4];
+      magnitude_signs<MK>(fabsf(z), tk, dm);
+      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);  // inverted below
+#pragma unroll
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]) ^ zb);
+      const float e = z - __builtin_copysignf(centroid_mag<MK>(ck, dm), z);
+      x[c] = e;
+      es = fmaf(e, e, es);
+      // keep the words and the sum current here (the compiler would otherwise
+      // defer them and hold every z and e alive)
+#pragma unroll
+      for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
+      asm volatile("" : "+v"(es));
+    }
+    kw[MK - 1][gg] = ~kw[MK - 1][gg];
+  }
+  const float gamma = sqrtf(es) * (zero ? 0.f : 1.f / kscale);
+  phase();
+  // QJL: z = [S e < 0] with S = H D2 H_n D1 (the positive factors drop out)
+  flip_signs<D>(x, sgn[kRoleSketch1]);
+  fwht_regs<D>(x);
+  flip_signs<D>(x, sgn[kRoleSketch2]);
+  fwht_regs<D>(x);
+  phase();
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    uint32_t q = 0u;
+#pragma unroll
+    for (int k = 31; k >= 0; --k) {
+      q = shift_in_sign(q, __float_as_uint(x[32 * gg + k]));
+      asm volatile("" : "+v"(q));
+    }
+    kw[MK][gg] = zero ? 0u : q;
+  }
+  if (zero) {
+#pragma unroll
+    for (int p = 0; p < MK; ++p)
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) kw[p][gg] = 0u;
+  }
+  uint8_t* kb = page_ok ? cv.k_pages + (size_t(my_phys) * H + h) * cv.key_block : nullptr;
+  if (page_ok) {
+    // token row: for each 32-coordinate group, the words of all planes
+    uint32_t wr[KWORDS];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+      for (int p = 0; p <= MK; ++p) wr[gg * (MK + 1) + p] = kw[p][gg];
+    uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * KWORDS * 4);
+    if constexpr (KWORDS % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < KWORDS / 4; ++q)
+        reinterpret_cast<uint4*>(dst)[q] = uint4{wr[4 * q], wr[4 * q + 1], wr[4 * q + 2], wr[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < KWORDS / 2; ++q) reinterpret_cast<uint2*>(dst)[q] = uint2{wr[2 * q], wr[2 * q + 1]};
+    }
+    *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * t) =
+        make_float2(zero ? 0.f : nu, gamma);
+  }
+
+  // ------------------------------------------------------------------ value
+  phase();
+  if (valid) {
+    load_row<D>(a.v_new, a.dtype, row, x);
+  } else {
+#pragma unroll
+    for (int c = 0; c < D; ++c) x[c] = 0.f;
+  }
+  if (in_window) store_f16_row<D>(cv.v_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
+  ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
+  const float vnu = sqrtf(ss);
+  const bool vzero = !(vnu >= kZeroNorm);
+  const float vscale = vzero ? 0.f : sqd * vnu;
+  float tv[NVT];
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * vscale;
+  phase();
+  flip_signs<D>(x, sgn[kRoleValueRot]);
+  fwht_regs<D>(x);
+  phase();
+  // plane masks of coordinate pairs, gathered at the lane of the pair:
+  // vm[p][parity][half] holds, at lane i, bits of coordinate 2 i + parity
+  const bool vbit_ok = valid && !vzero;
+  uint32_t vm[BV][2][2];
+#pragma unroll
+  for (int p = 0; p < BV; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) vm[p][q][0] = vm[p][q][1] = 0u;
+  static_for<0, D>([&](auto ci) {
+    constexpr int c = decltype(ci)::value;
+    const float z = x[c];
+    const uint32_t zb = __float_as_uint(z);
+    float dm[4];
+    magnitude_signs<BV>(fabsf(z), tv, dm);
+#pragma unroll
+    for (int p = 0; p < BV; ++p) {
+      const bool bit = p == BV - 1 ? int32_t(zb) >= 0 : int32_t(__float_as_uint(dm[p]) ^ zb) < 0;
+      const uint64_t m = __ballot(bit && vbit_ok);
+      vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
+      vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
+    }
+  });
+  if (page_ok) *reinterpret_cast<float*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block +
+                                         size_t(BV) * plane_bytes + 4 * t) = vzero ? 0.f : vnu;
+  // lane i < d/2 stores the words of coordinate pair i in each of the four pages
+  if (lane < D / 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (phys[j] < 0) continue;
+      const int pg0 = (P0 / P + j) * P;
+      if (pg0 >= new_len) continue;
+      const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+      if (keep16 == 0xffffu) continue;  // page holds no new token
+      const uint32_t keep = keep16 | (keep16 << 16);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[j]) * H + h) * cv.value_block) + lane * BV;
+      uint32_t wv[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        wv[p] = __builtin_amdgcn_perm(vm[p][1][j >> 1], vm[p][0][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+        if (keep) wv[p] = (dst[p] & keep) | wv[p];
+      }
+      if constexpr (BV == 4) {
+        *reinterpret_cast<uint4*>(dst) = uint4{wv[0], wv[1], wv[2], wv[3]};
+      } else if constexpr (BV == 2) {
+        *reinterpret_cast<uint2*>(dst) = uint2{wv[0], wv[1]};
+      } else {
+#pragma unroll
+        for (int p = 0; p < BV; ++p) dst[p] = wv[p];
+      }
+    }
+  }
+}
+
+template <int D, int MK>
+hipError_t launch_tok_bv(const AppendArgs& a, int units, hipStream_t st) {
+  switch (a.value_bits) {
+    case 1: hipLaunchKernelGGL((append_tok_kernel<D, MK, 1>), dim3(units), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((append_tok_kernel<D, MK, 2>), dim3(units), dim3(64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((append_tok_kernel<D, MK, 3>), dim3(units), dim3(64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((append_tok_kernel<D, MK, 4>), dim3(units), dim3(64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_tok(const AppendArgs& a, int units, hipStream_t st) {
+  switch (a.key_mse_bits) {
+    case 1: return launch_tok_bv<D, 1>(a, units, st);
+    case 2: return launch_tok_bv<D, 2>(a, units, st);
+    case 3: return launch_tok_bv<D, 3>(a, units, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D, int ROT>
 hipError_t launch(const AppendArgs& a, int units, hipStream_t st) {
   hipLaunchKernelGGL((append_kernel<D, ROT>), dim3(units), dim3(64), 0, st, a);
@@ -261,13 +686,33 @@ hipError_t launch(const AppendArgs& a, int units, hipStream_t st) {
 
 }  // namespace
 
-int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream) {
+// Below this many new tokens per sequence (decode-time appends) a wavefront
+// per token has the shorter latency: one lane would otherwise do a whole head
+// vector alone while the other 63 idle.
+constexpr int kTokenLaneMinNew = 32;
+
+int launch_append(const tq_config& cfg, const AppendArgs& args, int num_seqs, int max_new, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool dense = cfg.rotation == TQ_ROT_DENSE;
+  AppendArgs a = args;
+  const long long H = cfg.num_kv_heads;
+  if (!dense && (cfg.head_dim == 64 || cfg.head_dim == 128) && max_new >= kTokenLaneMinNew) {
+    // token-per-lane kernel: one wavefront per 64-position chunk a sequence's new tokens touch
+    a.parts = (max_new + 63) / 64 + 1;
+    const long long units = (long long)num_seqs * H * a.parts;
+    if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+    return cfg.head_dim == 64 ? launch_tok<64>(a, int(units), st) : launch_tok<128>(a, int(units), st);
+  }
+  // wavefront-per-token kernel: one wavefront per page, capped for huge prefills
+  int parts = (max_new + cfg.page_tokens - 1) / cfg.page_tokens + 1;
+  if (parts > 4096) parts = 4096;
+  a.parts = parts;
+  const long long units = (long long)num_seqs * H * parts;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (cfg.head_dim) {
-    case 64: return dense ? launch<64, TQ_ROT_DENSE>(a, total_units, st) : launch<64, TQ_ROT_FWHT>(a, total_units, st);
-    case 128: return dense ? launch<128, TQ_ROT_DENSE>(a, total_units, st) : launch<128, TQ_ROT_FWHT>(a, total_units, st);
-    case 256: return dense ? launch<256, TQ_ROT_DENSE>(a, total_units, st) : launch<256, TQ_ROT_FWHT>(a, total_units, st);
+    case 64: return dense ? launch<64, TQ_ROT_DENSE>(a, int(units), st) : launch<64, TQ_ROT_FWHT>(a, int(units), st);
+    case 128: return dense ? launch<128, TQ_ROT_DENSE>(a, int(units), st) : launch<128, TQ_ROT_FWHT>(a, int(units), st);
+    case 256: return dense ? launch<256, TQ_ROT_DENSE>(a, int(units), st) : launch<256, TQ_ROT_FWHT>(a, int(units), st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -82,7 +82,7 @@ struct AppendArgs {
   const int32_t* ctx_len_before;
   const int32_t* cu_new_tokens;
   int32_t num_seqs, dtype, key_mse_bits, value_bits;
-  int32_t parts;  // workers per (sequence, kv head)
+  int32_t parts;  // workers per (sequence, kv head), set by launch_append
 };
 
 struct DecodeArgs {
@@ -121,7 +121,7 @@ SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx);
 void build_params(const tq_config& cfg, uint8_t* blob);
 
 // Kernel launchers (one per .hip file); return hipError_t as int.
-int launch_append(const tq_config& cfg, const AppendArgs& a, int total_units, void* stream);
+int launch_append(const tq_config& cfg, const AppendArgs& a, int num_seqs, int max_new, void* stream);
 int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
 int decode_mfma_waves(const tq_config& cfg);  // wavefronts per (sequence, KV head, split) work item
