@@ -55,11 +55,34 @@ __host__ __device__ constexpr int prep_stride(int d, int mk) { return (num_plane
 template <int BITS>
 __device__ __forceinline__ uint32_t plane_word(const uint32_t* w, int i) {
   const int sub = odd_subset(BITS, i);
+  if (__builtin_popcount(sub) == 3) {
+    const int b0 = __builtin_ctz(sub), b1 = __builtin_ctz(sub & (sub - 1)), b2 = 31 - __builtin_clz(sub);
+    return __builtin_amdgcn_bitop3_b32(w[b0], w[b1], w[b2], kXor3);
+  }
   uint32_t x = 0;
 #pragma unroll
   for (int b = 0; b < BITS; ++b)
     if ((sub >> b) & 1) x ^= w[b];
   return x;
+}
+
+// The value operands of all plane products for one coordinate row: the
+// single-bit planes converted once, the three-bit products as XORs of those.
+template <int BITS>
+__device__ __forceinline__ void value_operands(const uint32_t (&w)[4], v8i (&op)[num_planes(BITS)]) {
+  v4i f[BITS];
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) f[b] = bits_to_fp4_pm1_dwords(w[b]);
+#pragma unroll
+  for (int p = 0; p < num_planes(BITS); ++p) {
+    const int sub = odd_subset(BITS, p);
+    if (__builtin_popcount(sub) == 1) {
+      op[p] = fp4_operand(f[__builtin_ctz(sub)]);
+    } else {
+      const int b0 = __builtin_ctz(sub), b1 = __builtin_ctz(sub & (sub - 1)), b2 = 31 - __builtin_clz(sub);
+      op[p] = fp4_operand(fp4_pm1_product3(f[b0], f[b1], f[b2]));
+    }
+  }
 }
 
 template <int CTRL>
@@ -141,8 +164,8 @@ __device__ __forceinline__ void block_sync() {
 template <int D, int MK, int ROT>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   constexpr int KP = num_planes(MK), KH = D / 128, T = 256;
-  __shared__ float q_rot[kMaxG * D];
-  __shared__ float q_sk[kMaxG * D];
+  __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
+  __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
   __shared__ float coef_k[16], qscale[2 * kMaxG];
   const int tid = threadIdx.x;
   const int H = a.cache.num_kv_heads;
@@ -171,26 +194,31 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     __syncthreads();
     block_fwht(q_sk, kMaxG, D, tid, T);
   } else {
-    // qt = Pi_K q;  qh = G qt
+    // qt = Pi_K q;  qh = G qt.  Thread i computes row i for the whole group,
+    // streaming the row in 16-byte pieces (each matrix entry is read once).
     const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
-    for (int i = tid; i < kMaxG * D; i += T) {
-      const float* row = pik + size_t(i % D) * D;
-      const float* x = q_rot + (i / D) * D;
-      float acc = 0.f;
-      for (int j = 0; j < D; ++j) acc = fmaf(row[j], x[j], acc);
-      q_sk[i] = acc;
-    }
+    auto gemv = [&](const float* m, const float* x, float* y) {
+      for (int i = tid; i < D; i += T) {
+        const float4* row = reinterpret_cast<const float4*>(m + size_t(i) * D);
+        float acc[kMaxG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int j4 = 0; j4 < D / 4; ++j4) {
+          const float4 mv = row[j4];
+#pragma unroll
+          for (int h = 0; h < kMaxG; ++h) {
+            const float4 xv = *reinterpret_cast<const float4*>(x + h * D + 4 * j4);
+            acc[h] = fmaf(mv.x, xv.x, fmaf(mv.y, xv.y, fmaf(mv.z, xv.z, fmaf(mv.w, xv.w, acc[h]))));
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) y[h * D + i] = acc[h];
+      }
+    };
+    gemv(pik, q_rot, q_sk);
     __syncthreads();
     for (int i = tid; i < kMaxG * D; i += T) q_rot[i] = q_sk[i];
     __syncthreads();
-    const float* gm = pik + size_t(D) * D;
-    for (int i = tid; i < kMaxG * D; i += T) {
-      const float* row = gm + size_t(i % D) * D;
-      const float* x = q_rot + (i / D) * D;
-      float acc = 0.f;
-      for (int j = 0; j < D; ++j) acc = fmaf(row[j], x[j], acc);
-      q_sk[i] = acc;
-    }
+    gemv(pik + size_t(D) * D, q_rot, q_sk);
     __syncthreads();
   }
   // Per head: power-of-two scales bringing the largest operand entry into
@@ -441,9 +469,12 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // working margin (scores, addresses) calibrated on the compiled kernels.
 // Two wavefronts per SIMD leave 256.
 constexpr int kRegBudget = 256;
+#ifndef TQ_REG_MARGIN
+#define TQ_REG_MARGIN 68
+#endif
 __host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds) {
   return num_planes(BV) * (D / 16 / NW) * 4 + (q_in_lds ? 0 : (num_planes(MK) + 1) * (D / 128) * 8) +
-         (8 / NW) * ((MK + 1) * (D / 128) + 3) + 2 * (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + 92;
+         (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + TQ_REG_MARGIN;
 }
 __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
   return (D / 16) % NW == 0 && 8 % NW == 0 && ((D / 16) / NW) % 2 == 0;
@@ -474,6 +505,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int PPW = 8 / NW;          // pages scored per wavefront per block
   constexpr int KW = (MK + 1) * KH;    // key words per lane per page
   constexpr int VW = (CBW / 2) * BV;   // value words per lane per page pair
+#ifndef TQ_PAGE_FENCE
+#define TQ_PAGE_FENCE 1
+#endif
+  constexpr bool kPageFence = TQ_PAGE_FENCE;
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
@@ -640,6 +675,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       if (a.logits && valid) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j];
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
+      if constexpr (kPageFence) {
+        if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the pages in flight
+      }
     }
     load_keys(tb + kBlock);
     // ---------------------------------------------- block maximum, weight range
@@ -710,10 +748,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           we[b] = __builtin_amdgcn_perm(B, A, 0x05040100u);  // A.lo | B.lo << 16 (even coordinate)
           wo[b] = __builtin_amdgcn_perm(B, A, 0x07060302u);  // A.hi | B.hi << 16 (odd coordinate)
         }
+        // even coordinate's planes, then the odd one's (keeps half the operands live)
+        {
+          v8i op[VP];
+          value_operands<BV>(we, op);
 #pragma unroll
-        for (int p = 0; p < VP; ++p) {
-          acc[p][2 * cp] = mfma_f4_f8(bits_to_fp4_pm1(plane_word<BV>(we, p)), wop, acc[p][2 * cp], scale_b);
-          acc[p][2 * cp + 1] = mfma_f4_f8(bits_to_fp4_pm1(plane_word<BV>(wo, p)), wop, acc[p][2 * cp + 1], scale_b);
+          for (int p = 0; p < VP; ++p) acc[p][2 * cp] = mfma_f4_f8(op[p], wop, acc[p][2 * cp], scale_b);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          v8i op[VP];
+          value_operands<BV>(wo, op);
+#pragma unroll
+          for (int p = 0; p < VP; ++p) acc[p][2 * cp + 1] = mfma_f4_f8(op[p], wop, acc[p][2 * cp + 1], scale_b);
         }
       }
     }

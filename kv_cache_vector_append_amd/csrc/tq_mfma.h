@@ -67,12 +67,31 @@ __device__ __forceinline__ v8i bits_to_fp4_affine(uint32_t w) {
   return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0), same element order.
-__device__ __forceinline__ v8i bits_to_fp4_pm1(uint32_t w) {
-  const v4i lo = {int(((w << 3) & 0x88888888u) | 0x22222222u), int(((w << 2) & 0x88888888u) | 0x22222222u),
-                  int(((w << 1) & 0x88888888u) | 0x22222222u), int((w & 0x88888888u) | 0x22222222u)};
+// v_bitop3_b32 truth tables (operands a, b, c stand for 0xF0, 0xCC, 0xAA)
+constexpr int kAndOr = 0xEA;  // (a & b) | c
+constexpr int kXor3 = 0x96;   // a ^ b ^ c
+
+// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0), same element order as
+// bits_to_fp4_affine: dword j = ((w << (3 - j)) & 0x88888888) | 0x22222222.
+__device__ __forceinline__ v4i bits_to_fp4_pm1_dwords(uint32_t w) {
+  return v4i{int(__builtin_amdgcn_bitop3_b32(w << 3, 0x88888888u, 0x22222222u, kAndOr)),
+             int(__builtin_amdgcn_bitop3_b32(w << 2, 0x88888888u, 0x22222222u, kAndOr)),
+             int(__builtin_amdgcn_bitop3_b32(w << 1, 0x88888888u, 0x22222222u, kAndOr)),
+             int(__builtin_amdgcn_bitop3_b32(w, 0x88888888u, 0x22222222u, kAndOr))};
+}
+// The +-1 encoding of the XOR of three bit words: XOR of their encodings (the
+// 1.0 magnitude bits of three operands XOR back to 1.0, the signs multiply).
+__device__ __forceinline__ v4i fp4_pm1_product3(const v4i& a, const v4i& b, const v4i& c) {
+  return v4i{int(__builtin_amdgcn_bitop3_b32(uint32_t(a[0]), uint32_t(b[0]), uint32_t(c[0]), kXor3)),
+             int(__builtin_amdgcn_bitop3_b32(uint32_t(a[1]), uint32_t(b[1]), uint32_t(c[1]), kXor3)),
+             int(__builtin_amdgcn_bitop3_b32(uint32_t(a[2]), uint32_t(b[2]), uint32_t(c[2]), kXor3)),
+             int(__builtin_amdgcn_bitop3_b32(uint32_t(a[3]), uint32_t(b[3]), uint32_t(c[3]), kXor3))};
+}
+// an fp4 operand occupies the low four registers; the upper four are not read
+__device__ __forceinline__ v8i fp4_operand(const v4i& lo) {
   return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
 }
+__device__ __forceinline__ v8i bits_to_fp4_pm1(uint32_t w) { return fp4_operand(bits_to_fp4_pm1_dwords(w)); }
 
 // Operand factor f_j for the element group j = (bit position) % 4 of the above.
 __host__ __device__ constexpr float fp4_affine_factor(int j) {
