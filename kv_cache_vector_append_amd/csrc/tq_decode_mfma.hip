@@ -586,12 +586,37 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint32_t v_off = uint32_t(((NCB * r16 + CBW * wvu) / 2) * BV * 4);
   typedef const int __attribute__((address_space(4))) const_int;
   const const_int* bt = (const const_int*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
-  const int last_page = t_end > 0 ? (t_end - 1) / kPage : 0;
-  // physical page of the page starting at pos0, -1 outside [t_begin, t_end) or when invalid
-  auto page_id = [&](int pos0) {
-    const int ph = bt[min(pos0 / kPage, last_page)];
-    return (pos0 < t_end && ph >= 0 && ph < cv.num_pages) ? ph : -1;
+  // Physical pages of the 8 pages of the block starting at tb (-1 outside
+  // [t_begin, t_end) or when invalid): one 32-byte scalar load when the
+  // block-table row holds 8 entries from there, else entry by entry.
+  int nid[8], nkid[PPW], ntb = 0;
+  auto fetch_ids = [&](int tb) {
+    const int p0 = tb / kPage;
+    if (p0 + 8 <= cv.max_pages_per_seq) {
+      typedef int ids8 __attribute__((ext_vector_type(8), aligned(4)));
+      typedef const ids8 __attribute__((address_space(4))) const_ids8;
+      const ids8 v = *(const const_ids8*)(bt + p0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) nid[j] = v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) nid[j] = p0 + j < cv.max_pages_per_seq ? bt[p0 + j] : -1;
+    }
+    // this wavefront's scored pages (its own scalar load: selecting from nid
+    // by wavefront would become a table in scratch memory)
+    if constexpr (NW == 1) {
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) nkid[j] = nid[j];
+    } else {
+      const int q0 = p0 + wvu * PPW;
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) nkid[j] = q0 + j < cv.max_pages_per_seq ? bt[q0 + j] : -1;
+    }
+    ntb = tb;
   };
+  // validity, applied where the ids are first used (so that the scalar loads
+  // stay in flight through the scores)
+  auto checked = [&](int id, int pos0) { return (pos0 < t_end && id >= 0 && id < cv.num_pages) ? id : -1; };
 
   v4f acc[VP][CBW];
 #pragma unroll
@@ -606,10 +631,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   float2 kn[PPW];
   float vn[PPW];
   uint32_t vw[2][VW];  // value words of the block
-  auto load_keys = [&](int tb) {
+  auto load_keys = [&]() {
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      kid[j] = page_id(tb + (wvu * PPW + j) * kPage);
+      kid[j] = checked(nkid[j], ntb + (wvu * PPW + j) * kPage);
       const int ph = max(kid[j], 0);
       const uint8_t* kb = kbase + size_t(ph) * kstride;
       const uint8_t* vb = vbase + size_t(ph) * vstride;
@@ -618,14 +643,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       vn[j] = *reinterpret_cast<const float*>(vb + vn_off);
     }
   };
-  auto load_values = [&](int tb) {
+  auto load_values = [&]() {
     // lane group g4 reads pages 2 g4 and 2 g4 + 1 of the block
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
-      const int p0 = max(page_id(tb + hp * kPage), 0);
-      const int p1 = max(page_id(tb + (2 + hp) * kPage), 0);
-      const int p2 = max(page_id(tb + (4 + hp) * kPage), 0);
-      const int p3 = max(page_id(tb + (6 + hp) * kPage), 0);
+      const int p0 = max(checked(nid[hp], ntb + hp * kPage), 0);
+      const int p1 = max(checked(nid[2 + hp], ntb + (2 + hp) * kPage), 0);
+      const int p2 = max(checked(nid[4 + hp], ntb + (4 + hp) * kPage), 0);
+      const int p3 = max(checked(nid[6 + hp], ntb + (6 + hp) * kPage), 0);
       int mine = p0;
       mine = g4 == 1 ? p1 : mine;
       mine = g4 == 2 ? p2 : mine;
@@ -635,8 +660,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   if (t_begin < t_end) {
-    load_keys(t_begin);
-    load_values(t_begin);
+    fetch_ids(t_begin);
+    load_keys();
+    load_values();
   }
   // wait here once for everything requested so far, so that the loop's own
   // waits only ever cover loads issued inside the loop
@@ -647,6 +673,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // the split's end they fall on page 0 and are not used), so that no wait
   // depends on a branch.
   for (int tb = t_begin; tb < t_end; tb += kBlock) {
+    fetch_ids(tb + kBlock);  // the next block's pages; their waits fall after the scores
     // ---------------------------------------------- scores of this wavefront's pages
     float sc[PPW], vnu[PPW];
     bool kok[PPW];
@@ -672,14 +699,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? a.scale * est : -INFINITY;
       vnu[j] = tok_ok ? vn[j] : 0.f;
-      if (a.logits && valid) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j];
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
       if constexpr (kPageFence) {
         if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the pages in flight
       }
     }
-    load_keys(tb + kBlock);
+    if (a.logits) {  // optional score dump (tests); one uniform branch per block
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) {
+        const int pos = tb + (wvu * PPW + j) * kPage + r16;
+        if (sc[j] != -INFINITY) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j];
+      }
+    }
+    load_keys();
     // ---------------------------------------------- block maximum, weight range
     loc_max = max16(loc_max);
     loc_vmax = max16(loc_vmax);
@@ -764,7 +797,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
     }
-    load_values(tb + kBlock);
+    load_values();
     block_sync<NW>();
   }
 
