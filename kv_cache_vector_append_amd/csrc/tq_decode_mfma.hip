@@ -50,7 +50,7 @@ __host__ __device__ constexpr int odd_subset(int bits, int i) {
 __host__ __device__ constexpr int num_planes(int bits) { return 1 << (bits - 1); }
 
 // bytes of one (sequence, kv head) entry of the query-operand region
-__host__ __device__ constexpr int prep_stride(int d, int mk) { return (num_planes(mk) + 1) * (d / 128) * 2048 + 64; }
+__host__ __device__ constexpr int prep_stride(int d, int mk) { return (num_planes(mk) + 1) * (d / 128) * 2048 + 256; }
 
 template <int BITS>
 __device__ __forceinline__ uint32_t plane_word(const uint32_t* w, int i) {
@@ -85,9 +85,11 @@ __device__ __forceinline__ void value_operands(const uint32_t (&w)[4], v8i (&op)
   }
 }
 
+// value of another lane of the same row (every pattern used reads inside the
+// row, so the bound control never applies); folds into the consuming add/max
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 // reductions over the 16 lanes of a row: quad butterflies, then half-row and row mirrors
 __device__ __forceinline__ float max16(float v) {
@@ -112,12 +114,13 @@ __device__ __forceinline__ float row_value(float v, int row) {  // value held by
   return row == 0 ? a0 : row == 1 ? a1 : row == 2 ? a2 : a3;
 }
 
-// power of two f with max_abs * f in (128, 256]; 1 when max_abs == 0
-__device__ __forceinline__ float fp8_range_scale(float max_abs) {
-  if (!(max_abs > 0.f)) return 1.f;
+// exponent e of the power of two 2^e with max_abs 2^e in (128, 256] (0 when
+// max_abs == 0), at most 114 so that 127 - e - 12 stays a valid E8M0 scale
+__device__ __forceinline__ int fp8_range_exp(float max_abs) {
+  if (!(max_abs > 0.f)) return 0;
   int e;
   frexpf(max_abs, &e);
-  return ldexpf(1.f, 8 - e);
+  return min(8 - e, 114);
 }
 
 // fp4 element e of a converted word comes from bit fp4_elem_bit(e); inverse:
@@ -161,41 +164,84 @@ __device__ __forceinline__ void block_sync() {
 }
 
 // ---------------------------------------------------------------------------- query operands
+// One workgroup per (sequence, kv head); wavefront h rotates and sketches query
+// head h of the GQA group in registers (FWHT variant) and reduces its operand
+// scale and affine constants; then the lane-major operand images are built in
+// LDS and copied out in 16-byte pieces.
 template <int D, int MK, int ROT>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
-  constexpr int KP = num_planes(MK), KH = D / 128, T = 256;
+  constexpr int KP = num_planes(MK), KH = D / 128, R = D / 64, T = 256;
+  static_assert(T == 64 * kMaxG, "one wavefront per query head of the group");
   __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
   __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
-  __shared__ float coef_k[16], qscale[2 * kMaxG];
-  const int tid = threadIdx.x;
+  __shared__ float coef_k[16], qscale[kMaxG];
+  __shared__ __attribute__((aligned(16))) uint8_t img[(KP + 1) * KH * 2048];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.cache.num_kv_heads;
   const int G = a.num_q_heads / H;
   const int s = blockIdx.x / H, hk = blockIdx.x % H;
   uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK);
-  if (tid < 16) coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef)[tid];
-  for (int i = tid; i < kMaxG * D; i += T) {
-    const int g = i / D;
-    q_rot[i] = g < G ? load_elem(a.q, a.q_dtype, (size_t(s) * a.num_q_heads + hk * G) * D + i) : 0.f;
-  }
-  __syncthreads();
+  // scores come out in base-2 logits: the softmax scale times log2(e) rides on
+  // both query operands, and the QJL constant sqrt(pi/2)/d on the sketch one
+  const float s2 = a.scale * 1.4426950408889634f;
+  const float s2q = s2 * kQjlConst / float(D);
+  const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
   if (ROT == TQ_ROT_FWHT) {
     // qt = H_n D_K q;  qh = H D2 H_n D1 qt
-    for (int i = tid; i < kMaxG * D; i += T) q_rot[i] = apply_sign(q_rot[i], sign_bit(a.params, kRoleKeyRot, i % D));
-    __syncthreads();
-    block_fwht(q_rot, kMaxG, D, tid, T);
-    for (int i = tid; i < kMaxG * D; i += T) {
-      q_rot[i] *= rsqrtf(float(D));
-      q_sk[i] = apply_sign(q_rot[i], sign_bit(a.params, kRoleSketch1, i % D));
+    // every global load first (one uniform dtype branch), so that they are in
+    // flight together
+    float x[R], y[R];
+    uint32_t sgk[R], sg1[R], sg2[R];
+    const size_t qb = (qrow0 + wv) * D + lane;
+    if (wv >= G) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = 0.f;
+    } else if (a.q_dtype == TQ_F32) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = static_cast<const float*>(a.q)[qb + r * 64];
+    } else {
+      uint16_t qbits[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) qbits[r] = static_cast<const uint16_t*>(a.q)[qb + r * 64];
+      const bool bf = a.q_dtype == TQ_BF16;
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = bf ? bf16_bits_to_float(qbits[r]) : f16_bits_to_float(qbits[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = r * 64 + lane;
+      sgk[r] = sign_bit(a.params, kRoleKeyRot, c);
+      sg1[r] = sign_bit(a.params, kRoleSketch1, c);
+      sg2[r] = sign_bit(a.params, kRoleSketch2, c);
+    }
+    if (tid < 16) coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef)[tid];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sgk[r]);
+    wave_fwht<R>(x, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      x[r] *= rsqrtf(float(D));
+      y[r] = apply_sign(x[r], sg1[r]);
+    }
+    wave_fwht<R>(y, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
+    wave_fwht<R>(y, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      q_rot[wv * D + r * 64 + lane] = x[r] * s2;
+      q_sk[wv * D + r * 64 + lane] = y[r] * s2q;
     }
     __syncthreads();
-    block_fwht(q_sk, kMaxG, D, tid, T);
-    for (int i = tid; i < kMaxG * D; i += T)
-      q_sk[i] = apply_sign(q_sk[i] * rsqrtf(float(D)), sign_bit(a.params, kRoleSketch2, i % D));
-    __syncthreads();
-    block_fwht(q_sk, kMaxG, D, tid, T);
   } else {
     // qt = Pi_K q;  qh = G qt.  Thread i computes row i for the whole group,
     // streaming the row in 16-byte pieces (each matrix entry is read once).
+    if (tid < 16) coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef)[tid];
+    for (int i = tid; i < kMaxG * D; i += T) {
+      const int g = i / D;
+      q_rot[i] = g < G ? load_elem(a.q, a.q_dtype, qrow0 * D + i) : 0.f;
+    }
+    __syncthreads();
     const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
     auto gemv = [&](const float* m, const float* x, float* y) {
       for (int i = tid; i < D; i += T) {
@@ -220,56 +266,83 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     __syncthreads();
     gemv(pik + size_t(D) * D, q_rot, q_sk);
     __syncthreads();
+    for (int i = tid; i < kMaxG * D; i += T) {
+      q_rot[i] *= s2;
+      q_sk[i] *= s2q;
+    }
+    __syncthreads();
   }
-  // Per head: power-of-two scales bringing the largest operand entry into
-  // (128, 256], and the constants of the affine fp4 encoding of the key bits
-  // (coordinate c falls in element group c % 4): the sums of the scaled
-  // operands over the coordinates with c % 4 < 3.  Tail floats: [0, 4) inverse
-  // key-plane scales, [4, 8) inverse QJL scales, [8, 12) key-plane constants,
-  // [12, 16) QJL constants.
-  if (tid < kMaxG) {
+  // Per head (wavefront wv): one power of two 2^e bringing the larger of its
+  // key-plane and QJL operands' largest entry into (128, 256] (the smaller
+  // operand keeps the four parts' precision far below the tolerance), undone
+  // by the score MFMA's per-row operand scale together with the part weight
+  // 16^-p; and the constants of the affine fp4 encoding of the key bits
+  // (coordinate c falls in element group c % 4): the sums of the operands over
+  // the coordinates with c % 4 < 3, which seed the accumulators.  Tail: int32
+  // [0, 16) E8M0 scales of rows 4 h + p; float [16, 20) key-plane constants,
+  // [20, 24) QJL constants.
+  {
     float csum = 0.f, cmax = 0.f;
+#pragma unroll
     for (int i = 0; i < KP; ++i) {
       csum += coef_k[odd_subset(MK, i)];
       cmax = fmaxf(cmax, fabsf(coef_k[odd_subset(MK, i)]));
     }
     float qm = 0.f, qh = 0.f, sm = 0.f, sh = 0.f;
-    for (int c = 0; c < D; ++c) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = r * 64 + lane;
       const float f = fabsf(fp4_affine_factor(c & 3));
-      qm = fmaxf(qm, f * fabsf(q_rot[tid * D + c]));
-      qh = fmaxf(qh, f * fabsf(q_sk[tid * D + c]));
+      const float xr = q_rot[wv * D + c], xs = q_sk[wv * D + c];
+      qm = fmaxf(qm, f * fabsf(xr));
+      qh = fmaxf(qh, f * fabsf(xs));
       if ((c & 3) != 3) {
-        sm += q_rot[tid * D + c];
-        sh += q_sk[tid * D + c];
+        sm += xr;
+        sh += xs;
       }
     }
-    qscale[tid] = fp8_range_scale(qm * cmax);
-    qscale[kMaxG + tid] = fp8_range_scale(qh);
-    float* tail = reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048);
-    tail[tid] = 1.f / qscale[tid];
-    tail[kMaxG + tid] = 1.f / qscale[kMaxG + tid];
-    tail[2 * kMaxG + tid] = sm * csum * qscale[tid];
-    tail[3 * kMaxG + tid] = sh * qscale[kMaxG + tid];
+    qm = wave_max(qm);
+    qh = wave_max(qh);
+    sm = wave_sum(sm);
+    sh = wave_sum(sh);
+    const int e = fp8_range_exp(fmaxf(qm * cmax, qh));
+    if (lane == 0) {
+      qscale[wv] = ldexpf(1.f, e);
+      int32_t* tail_i = reinterpret_cast<int32_t*>(dst + (KP + 1) * KH * 2048);
+      float* tail_f = reinterpret_cast<float*>(tail_i + 16);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) tail_i[4 * wv + p] = kScaleOne - e - 4 * p;
+      tail_f[wv] = sm * csum;
+      tail_f[kMaxG + wv] = sh;
+    }
   }
   __syncthreads();
-  // fp8 parts of f_j a_S qt (key planes) and of f_j qh (QJL) as lane-major
-  // operand images [plane][half] of rows 4 h + part.  Coordinate c sits in key word c / 32
-  // at bit c % 32; word wd feeds half (KH == 2 ? wd & 1 : 0) at K group
-  // (KH == 2 ? wd >> 1 : wd), fp4 element fp4_bit_elem(c % 32).
-  for (int i = tid; i < (KP + 1) * kMaxG * D; i += T) {
-    const int pl = i / (kMaxG * D), rem = i % (kMaxG * D), h = rem / D, c = rem % D;
-    const float f = fp4_affine_factor(c & 3);
-    const float x = pl < KP ? f * q_rot[h * D + c] * coef_k[odd_subset(MK, pl)] * qscale[h]
-                            : f * q_sk[h * D + c] * qscale[kMaxG + h];
-    const uint32_t parts = fp8_split4(x);
+  // Operand images [plane][half], rows 4 h + part, built in LDS and stored
+  // in 16-byte pieces.  Coordinate c sits in key word wd = c / 32 at bit
+  // c % 32; the word feeds half (KH == 2 ? wd & 1 : 0) at K group
+  // (KH == 2 ? wd >> 1 : wd), fp4 element fp4_bit_elem(c % 32).  Coordinates
+  // c and c + 4 (c % 8 < 4) land on adjacent bytes, so each thread splits such
+  // a pair at once and stores 16 bits per part row.
+  for (int i = tid; i < (KP + 1) * kMaxG * (D / 2); i += T) {
+    const int pl = i / (kMaxG * D / 2), rem = i % (kMaxG * D / 2), h = rem / (D / 2), cp = rem % (D / 2);
+    const int c = 8 * (cp >> 2) + (cp & 3);
+    const float* src = (pl < KP ? q_rot : q_sk) + h * D;
+    const float mul = fp4_affine_factor(c & 3) * qscale[h] * (pl < KP ? coef_k[odd_subset(MK, pl)] : 1.f);
+    uint32_t lo, hi;
+    fp8_split4_pair(src[c] * mul, src[c + 4] * mul, 0u, 0u, lo, hi);
     const int wd = c / 32;
     const int hf = KH == 2 ? (wd & 1) : 0;
     const int kg = KH == 2 ? (wd >> 1) : wd;
-    const int k = 32 * kg + fp4_bit_elem(c % 32);
-    uint8_t* img = dst + size_t(pl * KH + hf) * 2048;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) img[fp8_image_offset(h * 4 + p, k)] = uint8_t(parts >> (8 * p));
+    uint16_t* im = reinterpret_cast<uint16_t*>(img + (pl * KH + hf) * 2048 +
+                                               fp8_image_offset(4 * h, 32 * kg + fp4_bit_elem(c % 32)));
+    im[0] = uint16_t(lo);
+    im[8] = uint16_t(lo >> 16);
+    im[16] = uint16_t(hi);
+    im[24] = uint16_t(hi >> 16);
   }
+  __syncthreads();
+  for (int i = tid; i < (KP + 1) * KH * 128; i += T)
+    reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(img)[i];
 }
 
 // ---------------------------------------------------------------------------- recent-token window
@@ -482,21 +555,38 @@ __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
 __host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds) {
   return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds) <= kRegBudget;
 }
+// Wavefronts resident per SIMD.  With at most two value bits at d = 128 the
+// work of a block divides over four wavefronts that each fit in 128
+// registers, so four of them share a SIMD and hide each other's latencies;
+// the other variants need up to 256 registers and run two per SIMD.
+#ifndef TQ_SPLIT_OCC4
+#define TQ_SPLIT_OCC4 0
+#endif
+__host__ __device__ constexpr int split_occupancy(int D, int MK, int BV) {
+  return TQ_SPLIT_OCC4 && D == 128 && BV <= 2 ? 4 : 2;
+}
+// Variants where the estimate above is too optimistic (the compiled loop
+// spills at the estimated count) and the wavefront count that compiles clean.
+__host__ __device__ constexpr int split_waves_override(int D, int MK, int BV) {
+  return split_occupancy(D, MK, BV) == 4 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
+}
 // wavefronts per work item: the fewest whose registers fit two wavefronts per SIMD
 __host__ __device__ constexpr int split_waves(int D, int MK, int BV) {
-  return split_fits(D, MK, BV, 1, true) ? 1 : split_fits(D, MK, BV, 2, true) ? 2 : split_fits(D, MK, BV, 4, true) ? 4 : 8;
+  return split_waves_override(D, MK, BV) ? split_waves_override(D, MK, BV)
+       : split_fits(D, MK, BV, 1, true) ? 1 : split_fits(D, MK, BV, 2, true) ? 2 : split_fits(D, MK, BV, 4, true) ? 4 : 8;
 }
 // query operands stay in registers when they fit, else each MFMA reads them from LDS
 __host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV) {
-  return !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
+  return split_occupancy(D, MK, BV) == 4 ? false : !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
 }
 
 // Re-base a head's reference maximum only when a block's maximum exceeds it by
 // more than this (weights stay below e^20; fp32 sums keep their range).
-constexpr float kRebase = 20.f;
+constexpr float kRebase = 28.f;  // base-2 logits: weights stay below 2^28 of the reference
+constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, int MK, int BV, int NW, bool QL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
+template <int D, int MK, int BV, int NW, bool QL, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
   constexpr int KP = num_planes(MK);   // key plane products
   constexpr int VP = num_planes(BV);   // value plane products
   constexpr int KH = D / 128;          // 128-coordinate halves of the score contraction
@@ -568,11 +658,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       return qa[pl][hf];
     }
   };
-  const float* tail = reinterpret_cast<const float*>(qp + (KP + 1) * KH * 2048);
+  // per-row operand scales of the query images (lane r16 scales row r16) and
+  // the affine constants of head g4, which seed the score accumulators
+  const int32_t* tail_i = reinterpret_cast<const int32_t*>(qp + (KP + 1) * KH * 2048);
+  const float* tail_f = reinterpret_cast<const float*>(tail_i + 16);
   const bool head_ok = g4 < G;
-  const float inv_sm = tail[g4], inv_sq = tail[kMaxG + g4];
-  const float k_m = tail[2 * kMaxG + g4], k_q = tail[3 * kMaxG + g4];
-  const float qjl_c = kQjlConst / float(D);
+  const int sa = tail_i[r16];
+  const float k_m = tail_f[g4], k_q = tail_f[kMaxG + g4];
 
   // page addressing: uniform page base + constant per-lane offsets.  Page ids
   // come through the scalar data cache (uniform addresses in the constant
@@ -589,7 +681,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Physical pages of the 8 pages of the block starting at tb (-1 outside
   // [t_begin, t_end) or when invalid): one 32-byte scalar load when the
   // block-table row holds 8 entries from there, else entry by entry.
-  int nid[8], nkid[PPW], ntb = 0;
+  int nid[8], nkid[PPW];
   auto fetch_ids = [&](int tb) {
     const int p0 = tb / kPage;
     if (p0 + 8 <= cv.max_pages_per_seq) {
@@ -612,18 +704,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int j = 0; j < PPW; ++j) nkid[j] = q0 + j < cv.max_pages_per_seq ? bt[q0 + j] : -1;
     }
-    ntb = tb;
   };
   // validity, applied where the ids are first used (so that the scalar loads
-  // stay in flight through the scores)
-  auto checked = [&](int id, int pos0) { return (pos0 < t_end && id >= 0 && id < cv.num_pages) ? id : -1; };
+  // stay in flight through the scores); pages past the split's end need no
+  // test here, their tokens fail the position test
+  auto checked = [&](int id) { return uint32_t(id) < uint32_t(cv.num_pages) ? id : -1; };
 
   v4f acc[VP][CBW];
 #pragma unroll
   for (int p = 0; p < VP; ++p)
 #pragma unroll
     for (int c = 0; c < CBW; ++c) acc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference maximum of head g4 (score layout)
+  float m_ref = -1e30f;     // reference maximum of head g4 (score layout, base-2 logits); finite so
+                            // that exp2(-inf - m_ref) = 0
   float l_part = 0.f;       // this lane's share of head g4's denominator, relative to m_ref
 
   int kid[PPW];  // page ids of the scored pages of the block being loaded
@@ -634,23 +727,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto load_keys = [&]() {
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      kid[j] = checked(nkid[j], ntb + (wvu * PPW + j) * kPage);
+      kid[j] = checked(nkid[j]);
       const int ph = max(kid[j], 0);
       const uint8_t* kb = kbase + size_t(ph) * kstride;
       const uint8_t* vb = vbase + size_t(ph) * vstride;
-      load_words<KW>(kb + k_off, kw[j]);
-      kn[j] = *reinterpret_cast<const float2*>(kb + kn_off);
-      vn[j] = *reinterpret_cast<const float*>(vb + vn_off);
+      // uniform base + 32-bit lane offset, kept inside the loop so that the
+      // loads take the scalar-base addressing form (no 64-bit vector adds)
+      uint32_t ko = k_off, kno = kn_off, vno = vn_off;
+      asm volatile("" : "+v"(ko), "+v"(kno), "+v"(vno));
+      load_words<KW>(kb + ko, kw[j]);
+      kn[j] = *reinterpret_cast<const float2*>(kb + kno);
+      vn[j] = *reinterpret_cast<const float*>(vb + vno);
     }
   };
   auto load_values = [&]() {
     // lane group g4 reads pages 2 g4 and 2 g4 + 1 of the block
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
-      const int p0 = max(checked(nid[hp], ntb + hp * kPage), 0);
-      const int p1 = max(checked(nid[2 + hp], ntb + (2 + hp) * kPage), 0);
-      const int p2 = max(checked(nid[4 + hp], ntb + (4 + hp) * kPage), 0);
-      const int p3 = max(checked(nid[6 + hp], ntb + (6 + hp) * kPage), 0);
+      const int p0 = max(checked(nid[hp]), 0);
+      const int p1 = max(checked(nid[2 + hp]), 0);
+      const int p2 = max(checked(nid[4 + hp]), 0);
+      const int p3 = max(checked(nid[6 + hp]), 0);
       int mine = p0;
       mine = g4 == 1 ? p1 : mine;
       mine = g4 == 2 ? p2 : mine;
@@ -682,22 +779,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     float loc_max = -INFINITY, loc_vmax = 0.f;
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      v4f dm = {0.f, 0.f, 0.f, 0.f}, dq = {0.f, 0.f, 0.f, 0.f};
+      v4f dm = {k_m, 0.f, 0.f, 0.f}, dq = {k_q, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hf = 0; hf < KH; ++hf) {
         const uint32_t* w = kw[j] + hf * (MK + 1);
 #pragma unroll
-        for (int pl = 0; pl < KP; ++pl) dm = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm);
-        dq = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq);
+        for (int pl = 0; pl < KP; ++pl)
+          dm = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm, sa);
+        dq = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq, sa);
       }
       const int pos = tb + (wvu * PPW + j) * kPage + r16;
-      // dm[i], dq[i]: part i of head g4 for token r16
-      const float msum = fmaf(fmaf(fmaf(dm[3], 0.0625f, dm[2]), 0.0625f, dm[1]), 0.0625f, dm[0]) + k_m;
-      const float qsum = fmaf(fmaf(fmaf(dq[3], 0.0625f, dq[2]), 0.0625f, dq[1]), 0.0625f, dq[0]) + k_q;
-      const float est = kn[j].x * fmaf(kn[j].y * qjl_c, qsum * inv_sq, msum * inv_sm);
+      // dm[i], dq[i]: part i of head g4 for token r16, already in logit units
+      const float msum = (dm[0] + dm[1]) + (dm[2] + dm[3]);
+      const float qsum = (dq[0] + dq[1]) + (dq[2] + dq[3]);
+      const float est = kn[j].x * fmaf(kn[j].y, qsum, msum);
       const bool tok_ok = pos < t_end && kok[j];
       const bool valid = tok_ok && head_ok;
-      sc[j] = valid ? a.scale * est : -INFINITY;
+      sc[j] = valid ? est : -INFINITY;
       vnu[j] = tok_ok ? vn[j] : 0.f;
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
@@ -709,7 +807,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
         const int pos = tb + (wvu * PPW + j) * kPage + r16;
-        if (sc[j] != -INFINITY) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j];
+        if (sc[j] != -INFINITY) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j] * kLn2;
       }
     }
     load_keys();
@@ -730,10 +828,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     // re-base the reference maximum (rare): weights stay below e^kRebase
-    const bool rebase = blk_max > m_ref + kRebase || (m_ref == -INFINITY && blk_max > -INFINITY);
+    const bool rebase = blk_max > m_ref + kRebase;
     if (__any(rebase)) {
       const float m_new = rebase ? blk_max : m_ref;
-      const float r = m_new == m_ref ? 1.f : __expf(m_ref - m_new);
+      const float r = m_new == m_ref ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       l_part *= r;
       // value layout: column r16 = (head r16 / 4, part r16 % 4)
       const float rv = row_value(r, r16 >> 2);
@@ -747,23 +845,35 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     // the value MFMAs undo it through their E8M0 operand scale
     const float hd = blk_max - m_ref;  // <= kRebase, -inf for heads without tokens
     const float hmax = fmaxf(fmaxf(row_value(hd, 0), row_value(hd, 1)), fmaxf(row_value(hd, 2), row_value(hd, 3)));
-    const float bound = blk_vmax * __expf(hmax);
+    const float bound = blk_vmax * __builtin_amdgcn_exp2f(hmax);
     int e8 = 0;
     if (bound > 0.f) {
       frexpf(bound, &e8);
-      e8 = min(max(8 - e8, -120), 120);
+      e8 = min(max(8 - e8, -120), 115);
     }
     const float wscale = ldexpf(1.f, e8);
     const int scale_b = kScaleOne - e8;
+    // fp8 parts of the weights, two pages at a time, to rows 4 g4 + part of
+    // the weight image
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const float p = sc[j] == -INFINITY ? 0.f : __expf(sc[j] - m_ref);
-      l_part += p;
-      const uint32_t parts = fp8_split4(p * vnu[j] * wscale);
-      const int t = (wvu * PPW + j) * kPage + r16;
-      const int k = 32 * (t / 32) + fp4_bit_elem(t % 32);
+    for (int j = 0; j < PPW; j += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[j] - m_ref);  // 0 for sc = -inf
+      const float p1 = j + 1 < PPW ? __builtin_amdgcn_exp2f(sc[j + 1] - m_ref) : 0.f;
+      l_part += p0 + p1;
+      uint32_t lo, hi;
+      fp8_split4_pair(p0 * vnu[j] * wscale, j + 1 < PPW ? p1 * vnu[j + 1] * wscale : 0.f,
+                      __builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), lo, hi);
 #pragma unroll
-      for (int p4 = 0; p4 < 4; ++p4) w_img[fp8_image_offset(g4 * 4 + p4, k)] = uint8_t(parts >> (8 * p4));
+      for (int u = 0; u < 2 && j + u < PPW; ++u) {
+        const int t = (wvu * PPW + j + u) * kPage + r16;
+        uint8_t* o = w_img + fp8_image_offset(g4 * 4, 32 * (t / 32) + fp4_bit_elem(t % 32));
+        uint32_t l8 = lo >> (8 * u), h8 = hi >> (8 * u);
+        if (u) asm volatile("" : "+v"(l8), "+v"(h8));  // keeps the >> 16 below a byte-2 store
+        o[0] = uint8_t(l8);
+        o[16] = uint8_t(l8 >> 16);
+        o[32] = uint8_t(h8);
+        o[48] = uint8_t(h8 >> 16);
+      }
     }
     block_sync<NW>();
     // ---------------------------------------------- value tiles of this wavefront
@@ -814,7 +924,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   if (wv == 0 && r16 == 0 && head_ok) {
     float* w0 = ws + ((size_t(s) * a.num_q_heads + hk * G + g4) * nrec + split) * rec;
-    w0[0] = m_ref;
+    w0[0] = l > 0.f ? m_ref * kLn2 : -INFINITY;  // natural-log units for the merge
     w0[1] = l;
   }
   // values: planes combine in-lane, parts across the lane quad (columns 4h..4h+3)
@@ -844,17 +954,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Merge the compressed splits of one (sequence, query head) by log-sum-exp,
 // rotate their value sum back once, add the window's (already unrotated) sum,
-// normalise and store.  The splits' records are read in parallel: maxima and
-// denominators across threads, value sums per coordinate with several loads
-// in flight.
+// normalise and store.  FWHT variant: one wavefront per row, four rows per
+// workgroup -- the splits' maxima and denominators across lanes, the value
+// sums per coordinate (D / 64 per lane) with several loads in flight, the
+// inverse FWHT in registers.  Dense variant: one row per workgroup, one
+// coordinate per thread, the inverse rotation as a matrix-vector product
+// through LDS.
+template <int ROT>
+__host__ __device__ constexpr int combine_rows(int) { return ROT == TQ_ROT_DENSE ? 1 : 4; }
 template <int D, int ROT>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
-  constexpr int NWV = D / 64;
-  __shared__ float buf[D];
-  __shared__ float fsp[kMaxSplits + 1];  // split maxima, then their weights
-  __shared__ float red[2][NWV];
-  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
-  const size_t row = blockIdx.x;  // s * H_q + h
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
+  constexpr int R = D / 64;
+  constexpr int RPB = combine_rows<ROT>(0);
+  __shared__ float buf[ROT == TQ_ROT_DENSE ? D : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t row = size_t(blockIdx.x) * RPB + (RPB > 1 ? wv : 0);  // s * H_q + h
+  if (RPB > 1 && row >= size_t(a.num_seqs) * a.num_q_heads) return;  // whole wavefronts; no barrier on this path
   const int s = int(row / a.num_q_heads);
   const int rec = 2 + D, nrec = a.splits + 1;
   const float* ws = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.workspace) + part_offset) +
@@ -867,80 +982,104 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, size_t 
   L = min(L, min(cv.max_pages_per_seq * kPage, a.max_ctx));
   const int nc = cv.window > 0 ? max(0, L - cv.window) : L;
   const int ns = min(a.splits, (nc + a.split_tokens - 1) / a.split_tokens);
-  // maxima: all splits' in parallel
-  float mloc = -INFINITY;
-  for (int sp = c; sp <= ns; sp += D) {
-    const int idx = sp < ns ? sp : a.splits;  // the window's record last
-    const float m = ws[size_t(idx) * rec];
-    fsp[sp] = m;
-    mloc = fmaxf(mloc, m);
-  }
-  mloc = wave_max(mloc);
-  if (lane == 0) red[0][wv] = mloc;
-  __syncthreads();
-  float M = red[0][0];
-#pragma unroll
-  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[0][w]);
-  // weights and denominator
-  float lloc = 0.f;
-  for (int sp = c; sp <= ns; sp += D) {
-    const int idx = sp < ns ? sp : a.splits;
-    const float m = fsp[sp];
-    const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
-    fsp[sp] = f;
-    if (f != 0.f) lloc = fmaf(f, ws[size_t(idx) * rec + 1], lloc);
-  }
-  lloc = wave_sum(lloc);
-  if (lane == 0) red[1][wv] = lloc;
-  __syncthreads();
+  auto rec_of = [&](int sp) { return ws + size_t(sp < ns ? sp : a.splits) * rec; };  // the window's record last
+  // maximum and denominator over the records (every wavefront of the row alike)
+  float M = -INFINITY;
+  for (int sp = lane; sp <= ns; sp += 64) M = fmaxf(M, rec_of(sp)[0]);
+  M = wave_max(M);
   float l = 0.f;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) l += red[1][w];
-  // value sums: coordinate c over the splits, eight loads in flight
-  float ar = 0.f;
-  int sp = 0;
-  for (; sp + 8 <= ns; sp += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ws[size_t(sp + u) * rec + 2 + c];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) ar = fmaf(fsp[sp + u], v[u], ar);
+  for (int sp = lane; sp <= ns; sp += 64) {
+    const float m = rec_of(sp)[0];
+    if (m != -INFINITY) l = fmaf(__expf(m - M), rec_of(sp)[1], l);
   }
-  for (; sp < ns; ++sp) ar = fmaf(fsp[sp], ws[size_t(sp) * rec + 2 + c], ar);
-  const float fw = fsp[ns];
-  const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
-  buf[c] = ar;
-  __syncthreads();
-  float o;
-  if (ROT == TQ_ROT_FWHT) {
-    block_fwht(buf, 1, D, c, D);
-    o = apply_sign(buf[c] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c));
+  l = wave_sum(l);
+  auto weight = [&](int sp) {
+    const float m = ws[size_t(sp) * rec];
+    return m == -INFINITY ? 0.f : __expf(m - M);
+  };
+  const float fw = weight(a.splits);
+  if constexpr (ROT == TQ_ROT_FWHT) {
+    // compressed value sums, coordinates r * 64 + lane
+    float ar[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ar[r] = 0.f;
+    constexpr int B = 32 / R;  // splits per batch: 32 loads in flight per lane
+    int sp = 0;
+    for (; sp + B <= ns; sp += B) {
+      float f[B], v[B][R];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        f[u] = weight(sp + u);
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[u][r] = ws[size_t(sp + u) * rec + 2 + r * 64 + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) ar[r] = fmaf(f[u], v[u][r], ar[r]);
+    }
+    for (; sp < ns; ++sp) {
+      const float f = weight(sp);
+#pragma unroll
+      for (int r = 0; r < R; ++r) ar[r] = fmaf(f, ws[size_t(sp) * rec + 2 + r * 64 + lane], ar[r]);
+    }
+    wave_fwht<R>(ar, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = r * 64 + lane;
+      const float o = apply_sign(ar[r] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c));
+      const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
+      a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
+    }
   } else {
-    const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D;
-    float o4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int j = 0; j < D; j += 4)
+    const int c = tid;
+    float ar = 0.f;
+    if (c < D) {
+      int sp = 0;
+      for (; sp + 4 <= ns; sp += 4) {
+        float f[4], v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o4[u] = fmaf(piv[size_t(j + u) * D + c], buf[j + u], o4[u]);
-    o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+        for (int u = 0; u < 4; ++u) {
+          f[u] = weight(sp + u);
+          v[u] = ws[size_t(sp + u) * rec + 2 + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ar = fmaf(f[u], v[u], ar);
+      }
+      for (; sp < ns; ++sp) ar = fmaf(weight(sp), ws[size_t(sp) * rec + 2 + c], ar);
+      buf[c] = ar;
+    }
+    __syncthreads();
+    if (c < D) {
+      const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D;
+      float o4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int j = 0; j < D; j += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o4[u] = fmaf(piv[size_t(j + u) * D + c], buf[j + u], o4[u]);
+      const float o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+      const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
+      a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
+    }
   }
-  a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
 }
 
 template <int D, int MK, int BV, int ROT>
 hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
   constexpr int NW = split_waves(D, MK, BV);
   constexpr bool QL = split_q_in_lds(D, MK, BV);
+  constexpr int OCC = split_occupancy(D, MK, BV);
   const int H = a.cache.num_kv_heads;
   const size_t part_offset = decode_prep_bytes(D, a.num_seqs, H);
   hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT>), dim3(a.num_seqs * H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW), 0, st,
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW), 0, st,
                      a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, ROT>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, st, a,
+  const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
+  hipLaunchKernelGGL((decode_combine_kernel<D, ROT>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a,
                      part_offset);
   return hipGetLastError();
 }
@@ -959,16 +1098,19 @@ hipError_t dispatch_bits(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int decode_mfma_waves(const tq_config& cfg) {
+int decode_mfma_items(const tq_config& cfg) {
   const int d = cfg.head_dim, mk = cfg.key_bits - 1, bv = cfg.value_bits;
-  if (mk < 1 || mk > 3 || bv < 1 || bv > 4 || (d != 128 && d != 256)) return 1;
-  constexpr int w128[3][4] = {{split_waves(128, 1, 1), split_waves(128, 1, 2), split_waves(128, 1, 3), split_waves(128, 1, 4)},
-                              {split_waves(128, 2, 1), split_waves(128, 2, 2), split_waves(128, 2, 3), split_waves(128, 2, 4)},
-                              {split_waves(128, 3, 1), split_waves(128, 3, 2), split_waves(128, 3, 3), split_waves(128, 3, 4)}};
-  constexpr int w256[3][4] = {{split_waves(256, 1, 1), split_waves(256, 1, 2), split_waves(256, 1, 3), split_waves(256, 1, 4)},
-                              {split_waves(256, 2, 1), split_waves(256, 2, 2), split_waves(256, 2, 3), split_waves(256, 2, 4)},
-                              {split_waves(256, 3, 1), split_waves(256, 3, 2), split_waves(256, 3, 3), split_waves(256, 3, 4)}};
-  return d == 128 ? w128[mk - 1][bv - 1] : w256[mk - 1][bv - 1];
+  if (mk < 1 || mk > 3 || bv < 1 || bv > 4 || (d != 128 && d != 256)) return 2048;
+  // work items that fill every SIMD once: 1024 SIMDs x resident wavefronts / wavefronts per item
+#define TQ_ITEMS(D_, MK_, BV_) (1024 * split_occupancy(D_, MK_, BV_) / split_waves(D_, MK_, BV_))
+  constexpr int i128[3][4] = {{TQ_ITEMS(128, 1, 1), TQ_ITEMS(128, 1, 2), TQ_ITEMS(128, 1, 3), TQ_ITEMS(128, 1, 4)},
+                              {TQ_ITEMS(128, 2, 1), TQ_ITEMS(128, 2, 2), TQ_ITEMS(128, 2, 3), TQ_ITEMS(128, 2, 4)},
+                              {TQ_ITEMS(128, 3, 1), TQ_ITEMS(128, 3, 2), TQ_ITEMS(128, 3, 3), TQ_ITEMS(128, 3, 4)}};
+  constexpr int i256[3][4] = {{TQ_ITEMS(256, 1, 1), TQ_ITEMS(256, 1, 2), TQ_ITEMS(256, 1, 3), TQ_ITEMS(256, 1, 4)},
+                              {TQ_ITEMS(256, 2, 1), TQ_ITEMS(256, 2, 2), TQ_ITEMS(256, 2, 3), TQ_ITEMS(256, 2, 4)},
+                              {TQ_ITEMS(256, 3, 1), TQ_ITEMS(256, 3, 2), TQ_ITEMS(256, 3, 3), TQ_ITEMS(256, 3, 4)}};
+#undef TQ_ITEMS
+  return d == 128 ? i128[mk - 1][bv - 1] : i256[mk - 1][bv - 1];
 }
 
 size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads) {

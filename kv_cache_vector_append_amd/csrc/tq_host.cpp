@@ -229,7 +229,7 @@ SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
   const bool mfma = decode_mfma_supported(cfg);
   const int units = (num_seqs > 0 ? num_seqs : 1) * cfg.num_kv_heads;
   const int tile = mfma ? 128 : 64;
-  const int items = mfma ? 2048 / decode_mfma_waves(cfg) : 2048;
+  const int items = mfma ? decode_mfma_items(cfg) : 2048;
   const int max_tiles = (max_ctx + tile - 1) / tile;
   int splits = (items + units - 1) / units;
   if (splits > max_tiles) splits = max_tiles;

@@ -124,7 +124,7 @@ void build_params(const tq_config& cfg, uint8_t* blob);
 int launch_append(const tq_config& cfg, const AppendArgs& a, int num_seqs, int max_new, void* stream);
 int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
-int decode_mfma_waves(const tq_config& cfg);  // wavefronts per (sequence, KV head, split) work item
+int decode_mfma_items(const tq_config& cfg);  // (sequence, KV head, split) work items that fill the GPU once
 size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-operand region at the workspace start
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);

@@ -41,12 +41,16 @@ constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 constexpr int kScaleOne = 127;  // E8M0 exponent of 1.0
 
-// acc += A(fp8) x B(fp4)
-__device__ __forceinline__ v4f mfma_f8_f4(const v8i& a, const v8i& b, v4f acc) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp8, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+// Operand scales are E8M0 exponents (2^(s - 127)) held per lane: lane l
+// scales row (A) or column (B) l % 16 over its own K group l / 16 (measured on
+// the device), so a per-row or per-column power of two costs nothing.
+
+// acc += (A(fp8) * 2^(scale_a - 127)) x B(fp4)
+__device__ __forceinline__ v4f mfma_f8_f4(const v8i& a, const v8i& b, v4f acc, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp8, kFmtFp4, 0, scale_a, 0, kScaleOne);
 }
 
-// acc += A(fp4) x B(fp8) * 2^(scale_b - 127)   (scale_b: E8M0 exponent, the same in every lane)
+// acc += A(fp4) x (B(fp8) * 2^(scale_b - 127))
 __device__ __forceinline__ v4f mfma_f4_f8(const v8i& a, const v8i& b, v4f acc, int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, kFmtFp4, kFmtFp8, 0, kScaleOne, 0, scale_b);
 }
@@ -117,6 +121,34 @@ __device__ __forceinline__ uint32_t fp8_split4(float x) {
     r = (r - back) * 16.0f;
   }
   return out;
+}
+
+// The same four-part split for two values at once with the gfx950 scaled
+// conversions (fp8(r / s) one way, fp8 * s back, s a power of two): part p of x
+// is fp8(r_p 16^p) with r_0 = x and r_{p+1} = r_p - part_p 16^-p.  Byte order:
+// lo = x0 | y0 << 8 | x1 << 16 | y1 << 24, hi likewise with parts 2 and 3.
+// Both words of lo and hi are written, so they start from any caller values
+// (seed_lo, seed_hi): registers that are dead anyway avoid two moves.
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8_split4_pair(float x, float y, uint32_t seed_lo, uint32_t seed_hi, uint32_t& lo,
+                                                uint32_t& hi) {
+  v2s a = __builtin_bit_cast(v2s, seed_lo), b = __builtin_bit_cast(v2s, seed_hi);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, x, y, 1.0f, false);
+  v2f r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(__builtin_bit_cast(uint32_t, a), 1.0f, false);
+  x -= r.x;
+  y -= r.y;
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, x, y, 0.0625f, true);
+  r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(__builtin_bit_cast(uint32_t, a), 0.0625f, true);
+  x -= r.x;
+  y -= r.y;
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, x, y, 0.00390625f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(__builtin_bit_cast(uint32_t, b), 0.00390625f, false);
+  x -= r.x;
+  y -= r.y;
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, x, y, 0.000244140625f, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
 }
 
 }  // namespace tqi
