@@ -117,15 +117,22 @@ def calibration_copy():
 
 def _counter_sums(path, counter):
     """Per-dispatch values of `counter` from a rocprofv3 counter_collection.csv:
-    {kernel name: [value per dispatch]}."""
+    {kernel name: [(dispatch id, value), ...] in dispatch order}."""
     import csv
     out = {}
     with open(path) as f:
         for row in csv.DictReader(f):
             if row["Counter_Name"] != counter:
                 continue
-            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+            out.setdefault(row["Kernel_Name"], []).append((int(row["Dispatch_Id"]), float(row["Counter_Value"])))
+    for v in out.values():
+        v.sort()
     return out
+
+
+# dispatches of each kernel group taken from a counter run: the last ones, i.e.
+# the timed steps (the runs use --steps 2 --warmup 1; prefill dispatches come first)
+TRAFFIC_LAST_DISPATCHES = 2
 
 
 def write_traffic(fetch_csv, write_csv, workload):
@@ -134,7 +141,7 @@ def write_traffic(fetch_csv, write_csv, workload):
 
     def copy_kib(d):
         # the calibration kernel is the run's only bitwise-not
-        cands = [max(v) for k, v in d.items() if "bitwise_not" in k.lower() or "bitwisenot" in k.lower()]
+        cands = [max(x for _, x in v) for k, v in d.items() if "bitwise_not" in k.lower() or "bitwisenot" in k.lower()]
         return max(cands) if cands else None
 
     fk, wk = copy_kib(fetch), copy_kib(write)
@@ -147,15 +154,13 @@ def write_traffic(fetch_csv, write_csv, workload):
     for call, groups in KERNEL_MATCH.items():
         per_kernel = {}
         for alts in groups:
-            # the largest of the alternatives present (the one the timed calls launch)
-            best = None
-            for n in alts:
-                fv = [v for k, vals in fetch.items() if n in k for v in vals]
-                wv = [v for k, vals in write.items() if n in k for v in vals]
-                if fv and wv and (best is None or np.median(fv) > best[1][0]):
-                    best = (n, (float(np.median(fv)), float(np.median(wv))))
-            if best:
-                per_kernel[best[0]] = best[1]
+            # the group's last dispatches, whichever alternative they ran (the
+            # timed calls come after the prefill)
+            fv = sorted((i, v, n) for n in alts for k, vals in fetch.items() if n in k for i, v in vals)
+            wv = sorted((i, v, n) for n in alts for k, vals in write.items() if n in k for i, v in vals)
+            if fv and wv:
+                fl, wl = fv[-TRAFFIC_LAST_DISPATCHES:], wv[-TRAFFIC_LAST_DISPATCHES:]
+                per_kernel[fl[-1][2]] = (float(np.median([v for _, v, _ in fl])), float(np.median([v for _, v, _ in wl])))
         if len(per_kernel) != len(groups) or not f_scale or not w_scale:
             continue
         fb = sum(v[0] for v in per_kernel.values()) * f_scale
