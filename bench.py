@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 matrix-core peak (no sparsity)
+DENSE_SPLIT_PASSES = 3          # hi*hi + hi*lo + lo*hi fp16 products per contraction
 DEFAULT_WORKLOAD = "outlier_stress"
 
 
@@ -42,6 +44,12 @@ def record_bytes(w):
     key = w.key_bits * d // 8 + 8          # (b-1) d/8 codes + d/8 QJL signs + nu + gamma
     value = w.value_bits * d // 8 + 4      # b d/8 codes + nu
     return key, value
+
+
+def dense_append_flops(w, counts):
+    """Algorithmic flops of the dense-rotation append: three d x d products per
+    new token-head (Pi_K x, G e, Pi_V v), 2 d^2 flops each."""
+    return sum(counts) * w.num_kv_heads * 3 * 2 * w.head_dim ** 2
 
 
 def in_bytes(w):
@@ -93,11 +101,11 @@ SOURCES = {
 }
 KERNELS = {
     "decode": "tq_decode_attention (decode_prep + decode_split + decode_combine)",
-    "append": "tq_quantize_append (append_tok_kernel or append_kernel)",
+    "append": "tq_quantize_append (append_tok_kernel, append_dense_kernel or append_kernel)",
 }
 # rocprofv3 kernel names of each call's kernels (an append launches one of the two)
 KERNEL_MATCH = {"decode": (("decode_prep_kernel",), ("decode_split_kernel",), ("decode_combine_kernel",)),
-                "append": (("append_tok_kernel", "append_kernel<"),)}
+                "append": (("append_tok_kernel", "append_dense_kernel", "append_kernel<"),)}
 CALIBRATION_BYTES = 1 << 30
 
 
@@ -422,6 +430,15 @@ def main(argv=None):
                 "kernel": KERNELS[dom],
                 "algorithmic_bytes_per_launch": int(c["bytes"]), "avg_launch_ms": round(c["ms"], 5),
                 "source_hash": src_hash}
+    if dom == "append" and w.rotation == "dense":
+        # the dense rotation's append is a GEMM on the matrix cores
+        flops = dense_append_flops(w, r["app_counts"])
+        tflops = flops / (c["ms"] / 1e3) / 1e12
+        roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": int(flops),
+                         "executed_frac": round(DENSE_SPLIT_PASSES * tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                         "hbm_achieved_GBs": round(achieved, 2)})
     other = [k for k in calls if k != dom][0]
     oc = calls[other]
     line = {

@@ -10,11 +10,13 @@
 //   pack the bit-planes into page block_table[slot][pos / 16], slot pos % 16,
 //   and copy the last `window` tokens to the fp16 ring.
 //
-// Two kernels:
+// Three kernels:
 //  * append_tok_kernel (FWHT rotation, d = 64 or 128, appends of 32 or more
 //    tokens per sequence): a lane per token, everything in registers; see the
 //    comment above it.
-//  * append_kernel (the dense rotation, d = 256, and short appends): one
+//  * append_dense_kernel (dense rotation, d = 128 or 256): GEMMs of 64-token
+//    tiles on the matrix cores; see the comment above it.
+//  * append_kernel (d = 256 FWHT, dense d = 64, and short appends): one
 //    64-lane wavefront per (sequence, kv head, part); the part strides over the
 //    pages the sequence's new tokens touch, so a page is only ever written by
 //    one wavefront in a call.  Lanes hold coordinates (lane l owns coordinates
@@ -656,6 +658,405 @@ __global__ __launch_bounds__(64) void append_tok_kernel(AppendArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense-rotation append on the matrix cores (d = 128 or 256).
+//
+// One workgroup of four wavefronts takes 64 consecutive positions (four pages)
+// of one (sequence, kv head).  The three products of the dense variant,
+// y = Pi_K x / nu, the QJL projection w = G e and y_V = Pi_V v / nu_V, are
+// GEMMs over the 64 tokens, out[n][t] = sum_k M[n][k] X[t][k], on
+// v_mfma_f32_16x16x32_f16: A = rows of M (wavefront q owns the output
+// coordinates q d/4 .. (q+1) d/4 - 1 and reads them from the fp16 split in the
+// parameter blob, so every matrix entry is read once per tile), B = the token
+// rows staged in LDS.  fp32 accuracy from fp16 operands: both sides are split
+// hi + lo and hi*hi + hi*lo + lo*hi are accumulated in fp32 (the dropped lo*lo
+// term is below 2^-22 of each product).  The matrix cores flush fp16
+// subnormals, so the operands are scaled until only negligible lo pieces fall
+// below 2^-14: token rows by 2^10 / nu and the rotations by 2^10, so the
+// products are 2^20 y (thresholds and centroids scaled alike); the residual
+// enters the sketch as 2^12 e and G as 2^8 G (signs only come out).
+//
+// One [64 tokens][d] LDS block holds in turn: the token rows as fp16 pieces
+// ([8 hi][8 lo] per 8 coordinates), the fp32 products, the residuals as fp16
+// pieces (each written over its own fp32 source), the fp32 projections, and
+// the same for the values.  Between the GEMMs each wavefront takes a token per
+// lane over its quarter of the coordinates and makes the same code decisions
+// as the token-per-lane kernel.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr float kRowScale = 1024.f;                 // token rows: 2^10 x / nu
+constexpr float kOutScale = 1024.f * 1024.f;        // rotation products: 2^20 y
+constexpr float kResidualScale = 1.f / 256.f;       // sketch operand: 2^12 e
+template <int D>
+struct DenseTile {
+  static constexpr int T = 64;             // positions per workgroup
+  static constexpr int ROWB = D * 4 + 16;  // bytes per LDS row, padded against bank conflicts
+  static constexpr int Q = D / 4;          // coordinates per wavefront
+  static constexpr int CT = Q / 16;        // 16-coordinate tiles per wavefront
+  static constexpr int KS = D / 32;        // K steps of the GEMM
+};
+
+// out[n][t] for the wavefront's coordinates and all 64 tokens, accumulated in
+// acc[ct][tt] (lane l, element i: coordinate q d/4 + 16 ct + 4 (l / 16) + i,
+// token 16 tt + l % 16).  A and B place K index 32 ks + 8 g + e at element e of
+// lane group g, so the pairing holds whatever the instruction's K order.
+template <int D>
+__device__ __forceinline__ void dense_gemm(const _Float16* mhi, const _Float16* mlo, const uint8_t* buf, int q,
+                                           int lane, f4v (&acc)[DenseTile<D>::CT][4]) {
+  using DT = DenseTile<D>;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < DT::CT; ++ct)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[ct][tt] = f4v{0.f, 0.f, 0.f, 0.f};
+  h8v ah[2][DT::CT], al[2][DT::CT];
+  auto load_a = [&](int ks, int slot) {
+#pragma unroll
+    for (int ct = 0; ct < DT::CT; ++ct) {
+      const size_t off = size_t(q * DT::Q + 16 * ct + r16) * D + 32 * ks + 8 * g;
+      ah[slot][ct] = *reinterpret_cast<const h8v*>(mhi + off);
+      al[slot][ct] = *reinterpret_cast<const h8v*>(mlo + off);
+    }
+  };
+  load_a(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < DT::KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < DT::KS) load_a(ks + 1, cur ^ 1);
+    h8v bh[4], bl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint8_t* p = buf + (16 * tt + r16) * DT::ROWB + (4 * ks + g) * 32;
+      bh[tt] = *reinterpret_cast<const h8v*>(p);
+      bl[tt] = *reinterpret_cast<const h8v*>(p + 16);
+    }
+#pragma unroll
+    for (int ct = 0; ct < DT::CT; ++ct)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[cur][ct], bh[tt], acc[ct][tt], 0, 0, 0);
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[cur][ct], bl[tt], acc[ct][tt], 0, 0, 0);
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[cur][ct], bh[tt], acc[ct][tt], 0, 0, 0);
+      }
+  }
+}
+
+// The products as fp32 rows [token][coordinate] of the LDS block.
+template <int D>
+__device__ __forceinline__ void dense_store(const f4v (&acc)[DenseTile<D>::CT][4], uint8_t* buf, int q, int lane) {
+  using DT = DenseTile<D>;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < DT::CT; ++ct)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      *reinterpret_cast<f4v*>(buf + (16 * tt + r16) * DT::ROWB + (q * DT::Q + 16 * ct + 4 * g) * 4) = acc[ct][tt];
+}
+
+// 8 values as fp16 pieces [8 hi][8 lo] at p (32 bytes).  Each value is pinned
+// as the fp32 number it is first: otherwise the product that produced it can
+// be contracted into the lo computation, whose hi would then be rounded from
+// the exact product while the stored hi is rounded from the fp32 one.
+__device__ __forceinline__ void store_pieces(uint8_t* p, const float (&v)[8]) {
+#pragma clang fp contract(off)
+  h8v hi, lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = v[e];
+    asm volatile("" : "+v"(x));
+    hi[e] = _Float16(x);
+    lo[e] = _Float16(x - float(hi[e]));
+  }
+  *reinterpret_cast<h8v*>(p) = hi;
+  *reinterpret_cast<h8v*>(p + 16) = lo;
+}
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int D, int MK, int BV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void append_dense_kernel(AppendArgs a) {
+  using DT = DenseTile<D>;
+  constexpr int P = 16, T = DT::T, Q = DT::Q, LPT = D / 8, TPP = 64 / LPT;
+  constexpr int NKT = (1 << (MK - 1)) - 1 > 0 ? (1 << (MK - 1)) - 1 : 1, NKC = 1 << (MK - 1);
+  constexpr int NVT = (1 << (BV - 1)) - 1 > 0 ? (1 << (BV - 1)) - 1 : 1;
+  constexpr int NGQ = Q / 32;            // 32-coordinate key groups per wavefront
+  constexpr int KWORDS = (D / 32) * (MK + 1);
+  __shared__ __attribute__((aligned(16))) uint8_t buf[T * DT::ROWB];
+  __shared__ float nrm[T], esum[4][T];
+  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
+  const CacheView& cv = a.cache;
+  const int H = cv.num_kv_heads, W = cv.window;
+  int unit = blockIdx.x;
+  const int chunk = unit % a.parts;
+  unit /= a.parts;
+  const int h = unit % H;
+  const int s = unit / H;
+  if (s >= a.num_seqs) return;
+  const int slot = a.seq_slots[s];
+  if (slot < 0 || slot >= cv.max_seqs) return;
+  const int start = a.ctx_len_before[s];
+  const int b0 = a.cu_new_tokens[s];
+  const int n = a.cu_new_tokens[s + 1] - b0;
+  if (n <= 0 || start < 0) return;
+  const int new_len = start + n;
+  const int P0 = (start / T + chunk) * T;
+  if (P0 >= new_len) return;  // uniform: no barrier has been reached
+
+  const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
+  int phys[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pg = P0 / P + j;
+    const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
+    phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
+  }
+  const const_f32* prm = (const const_f32*)a.params;
+  const _Float16* m16 = reinterpret_cast<const _Float16*>(a.params + dense16_offset(D, 0));
+  const size_t mm = size_t(D) * D;  // halves per fp16 matrix
+  const size_t plane_bytes = size_t(P) * D / 8;
+
+  // token rows [P0, P0 + 64) of src into the LDS block as fp16 pieces of
+  // 2^10 x / nu; norms to nrm (0 outside [start, new_len)); fp16 ring copies of
+  // window rows.  Wavefront q stages tokens 16 q .. 16 q + 15, LPT lanes per row.
+  auto stage = [&](const void* src, uint16_t* ring) {
+    constexpr int NP = 16 / TPP;  // passes
+    // every pass's 8 elements first (one uniform dtype branch), so that the
+    // loads are in flight together
+    uint32_t raw[NP][8];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
+      const int pos = P0 + t;
+      const size_t e0 = ((size_t(b0) + (pos - start)) * H + h) * D + 8 * sub;
+      const bool valid = pos >= start && pos < new_len;
+      if (a.dtype == TQ_F32) {
+        const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const float*>(src) + e0);
+        const uint4 u = valid ? p4[0] : uint4{0u, 0u, 0u, 0u}, v = valid ? p4[1] : uint4{0u, 0u, 0u, 0u};
+        raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
+        raw[pass][4] = v.x; raw[pass][5] = v.y; raw[pass][6] = v.z; raw[pass][7] = v.w;
+      } else {
+        const uint4 u = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e0)
+                              : uint4{0u, 0u, 0u, 0u};
+        raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
+      const int pos = P0 + t;
+      const bool valid = pos >= start && pos < new_len;
+      float x[8];
+      if (a.dtype == TQ_F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(raw[pass][e]);
+      } else if (a.dtype == TQ_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = __uint_as_float(raw[pass][i] << 16);
+          x[2 * i + 1] = __uint_as_float(raw[pass][i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = f16_bits_to_float(uint16_t(raw[pass][i] & 0xffffu));
+          x[2 * i + 1] = f16_bits_to_float(uint16_t(raw[pass][i] >> 16));
+        }
+      }
+      if (valid && W > 0 && pos >= new_len - W) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w4[i] = uint32_t(float_to_f16_bits(x[2 * i])) | (uint32_t(float_to_f16_bits(x[2 * i + 1])) << 16);
+        *reinterpret_cast<uint4*>(ring + ((size_t(slot) * H + h) * W + (pos % W)) * D + 8 * sub) =
+            uint4{w4[0], w4[1], w4[2], w4[3]};
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+      for (int o = 1; o < LPT; o <<= 1) ss += __shfl_xor(ss, o);
+      const float nu = sqrtf(ss);
+      const float sc = nu >= kZeroNorm ? kRowScale / nu : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= sc;
+      store_pieces(buf + t * DT::ROWB + 32 * sub, x);
+      if (sub == 0) nrm[t] = valid && nu >= kZeroNorm ? nu : 0.f;
+    }
+  };
+  auto gemm_to_rows = [&](int m) {
+    f4v acc[DT::CT][4];
+    block_barrier();  // rows staged
+    dense_gemm<D>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc);
+    block_barrier();  // every wavefront has read the rows
+    dense_store<D>(acc, buf, q, lane);
+    block_barrier();  // products visible
+  };
+  // this lane's token, 32 coordinates of this wavefront's quarter
+  float z[32];
+  auto read_group = [&](int gg) {
+#pragma unroll
+    for (int c = 0; c < 32; c += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(buf + lane * DT::ROWB + (q * Q + 32 * gg + c) * 4);
+      z[c] = v.x; z[c + 1] = v.y; z[c + 2] = v.z; z[c + 3] = v.w;
+    }
+  };
+
+  const int t = lane, pos = P0 + t;
+  const bool valid = pos >= start && pos < new_len;
+  const int pj = t >> 4, ts = t & 15;
+  const bool page_ok = valid && phys[pj] >= 0;
+
+  // ------------------------------------------------------------------ key
+  stage(a.k_new, cv.k_window);
+  gemm_to_rows(0);
+  const float nu = nrm[t];
+  const bool zero = !(nu > 0.f);
+  float tk[NKT], ck[NKC];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kOutScale;
+#pragma unroll
+  for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kOutScale;
+  uint32_t kw[MK + 1][NGQ];
+  float es = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < NGQ; ++gg) {
+    read_group(gg);
+#pragma unroll
+    for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
+#pragma unroll
+    for (int k = 31; k >= 0; --k) {
+      const int c = k;
+      const float zz = z[c];
+      const uint32_t zb = __float_as_uint(zz);
+      float dm[4];
+      magnitude_signs<MK>(fabsf(zz), tk, dm);
+      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);  // inverted below
+#pragma unroll
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]) ^ zb);
+      const float e = zz - __builtin_copysignf(centroid_mag<MK>(ck, dm), zz);
+      z[c] = e;
+      es = fmaf(e, e, es);
+      // keep the words and the sum current (deferred, every decision would stay live)
+#pragma unroll
+      for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
+      asm volatile("" : "+v"(es));
+      if ((k & 7) == 0) {  // the 8 residuals of this block (as 2^12 e), over their fp32 source
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = z[c + i] * kResidualScale;
+        store_pieces(buf + t * DT::ROWB + (q * Q + 32 * gg + c) * 4, v);
+      }
+    }
+    kw[MK - 1][gg] = ~kw[MK - 1][gg];
+  }
+  esum[q][t] = es;
+  // QJL: signs of w = G e
+  gemm_to_rows(1);
+#pragma unroll
+  for (int gg = 0; gg < NGQ; ++gg) {
+    read_group(gg);
+    uint32_t qb = 0u;
+#pragma unroll
+    for (int k = 31; k >= 0; --k) qb = shift_in_sign(qb, __float_as_uint(z[k]));
+    kw[MK][gg] = qb;
+  }
+  if (page_ok) {
+    uint8_t* kb = cv.k_pages + (size_t(phys[pj]) * H + h) * cv.key_block;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(ts) * KWORDS * 4) + q * NGQ * (MK + 1);
+#pragma unroll
+    for (int gg = 0; gg < NGQ; ++gg)
+#pragma unroll
+      for (int p = 0; p <= MK; ++p) dst[gg * (MK + 1) + p] = zero ? 0u : kw[p][gg];
+    if (q == 0) {
+      const float gamma = zero ? 0.f : sqrtf(esum[0][t] + esum[1][t] + esum[2][t] + esum[3][t]) * (1.f / kOutScale);
+      *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * ts) = make_float2(zero ? 0.f : nu, gamma);
+    }
+  }
+  block_barrier();  // key products consumed, norms read
+
+  // ------------------------------------------------------------------ value
+  stage(a.v_new, cv.v_window);
+  gemm_to_rows(2);
+  const float vnu = nrm[t];
+  const bool vbit_ok = valid && vnu > 0.f;
+  float tv[NVT];
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * kOutScale;
+  // plane masks of this wavefront's coordinate pairs, at the lane of the pair
+  uint32_t vm[BV][2][2];
+#pragma unroll
+  for (int p = 0; p < BV; ++p)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) vm[p][r][0] = vm[p][r][1] = 0u;
+  static_for<0, Q>([&](auto ci) {
+    constexpr int c = decltype(ci)::value;
+    if constexpr (c % 32 == 0) read_group(c / 32);
+    const float zz = z[c % 32];
+    const uint32_t zb = __float_as_uint(zz);
+    float dm[4];
+    magnitude_signs<BV>(fabsf(zz), tv, dm);
+#pragma unroll
+    for (int p = 0; p < BV; ++p) {
+      const bool bit = p == BV - 1 ? int32_t(zb) >= 0 : int32_t(__float_as_uint(dm[p]) ^ zb) < 0;
+      const uint64_t m = __ballot(bit && vbit_ok);
+      vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
+      vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
+    }
+  });
+  if (page_ok && q == 0)
+    *reinterpret_cast<float*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block + size_t(BV) * plane_bytes +
+                              4 * ts) = vbit_ok ? vnu : 0.f;
+  // lane i < Q / 2 stores the words of coordinate pair q Q / 2 + i in each page
+  if (lane < Q / 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (phys[j] < 0) continue;
+      const int pg0 = (P0 / P + j) * P;
+      if (pg0 >= new_len) continue;
+      const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+      if (keep16 == 0xffffu) continue;  // page holds no new token
+      const uint32_t keep = keep16 | (keep16 << 16);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[j]) * H + h) * cv.value_block) +
+                      (q * Q / 2 + lane) * BV;
+      uint32_t wv[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        wv[p] = __builtin_amdgcn_perm(vm[p][1][j >> 1], vm[p][0][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+        if (keep) wv[p] = (dst[p] & keep) | wv[p];
+      }
+#pragma unroll
+      for (int p = 0; p < BV; ++p) dst[p] = wv[p];
+    }
+  }
+}
+
+template <int D, int MK>
+hipError_t launch_dense_bv(const AppendArgs& a, int units, hipStream_t st) {
+  switch (a.value_bits) {
+    case 1: hipLaunchKernelGGL((append_dense_kernel<D, MK, 1>), dim3(units), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((append_dense_kernel<D, MK, 2>), dim3(units), dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((append_dense_kernel<D, MK, 3>), dim3(units), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((append_dense_kernel<D, MK, 4>), dim3(units), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dense(const AppendArgs& a, int units, hipStream_t st) {
+  switch (a.key_mse_bits) {
+    case 1: return launch_dense_bv<D, 1>(a, units, st);
+    case 2: return launch_dense_bv<D, 2>(a, units, st);
+    case 3: return launch_dense_bv<D, 3>(a, units, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D, int MK>
 hipError_t launch_tok_bv(const AppendArgs& a, int units, hipStream_t st) {
   switch (a.value_bits) {
@@ -690,12 +1091,23 @@ hipError_t launch(const AppendArgs& a, int units, hipStream_t st) {
 // per token has the shorter latency: one lane would otherwise do a whole head
 // vector alone while the other 63 idle.
 constexpr int kTokenLaneMinNew = 32;
+// Dense rotation: the matrix-core kernel at any append size (even a single
+// token's tile costs less than the three d x d GEMVs of the wavefront-per-token
+// kernel, which stream the matrices with long dependent load chains).
+constexpr int kDenseMatrixMinNew = 1;
 
 int launch_append(const tq_config& cfg, const AppendArgs& args, int num_seqs, int max_new, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool dense = cfg.rotation == TQ_ROT_DENSE;
   AppendArgs a = args;
   const long long H = cfg.num_kv_heads;
+  if (dense && (cfg.head_dim == 128 || cfg.head_dim == 256) && max_new >= kDenseMatrixMinNew) {
+    // matrix-core kernel: one workgroup per 64-position chunk a sequence's new tokens touch
+    a.parts = (max_new + 63) / 64 + 1;
+    const long long units = (long long)num_seqs * H * a.parts;
+    if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+    return cfg.head_dim == 128 ? launch_dense<128>(a, int(units), st) : launch_dense<256>(a, int(units), st);
+  }
   if (!dense && (cfg.head_dim == 64 || cfg.head_dim == 128) && max_new >= kTokenLaneMinNew) {
     // token-per-lane kernel: one wavefront per 64-position chunk a sequence's new tokens touch
     a.parts = (max_new + 63) / 64 + 1;

@@ -1053,7 +1053,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
     if (c < D) {
       const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D;
       float o4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 8  // 32 matrix rows in flight per thread
       for (int j = 0; j < D; j += 4)
 #pragma unroll
         for (int u = 0; u < 4; ++u) o4[u] = fmaf(piv[size_t(j + u) * D + c], buf[j + u], o4[u]);

@@ -266,6 +266,14 @@ void build_params(const tq_config& cfg, uint8_t* blob) {
       std::vector<double> g = gaussian(cfg.seed, roles[m], d, d);
       if (m != 1) g = haar_from_gaussian(std::move(g), d);
       for (size_t i = 0; i < size_t(d) * d; ++i) dst[size_t(m) * d * d + i] = float(g[i]);
+      // fp16 hi / lo split of the scaled fp32 matrix for the matrix cores
+      _Float16* hi = reinterpret_cast<_Float16*>(blob + dense16_offset(d, m));
+      _Float16* lo = hi + size_t(d) * d;
+      for (size_t i = 0; i < size_t(d) * d; ++i) {
+        const float v = dst[size_t(m) * d * d + i] * kDense16Scale[m];
+        hi[i] = _Float16(v);
+        lo[i] = _Float16(v - float(hi[i]));
+      }
     }
   }
 }

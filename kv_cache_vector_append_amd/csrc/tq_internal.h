@@ -20,7 +20,12 @@ namespace tqi {
 //   [384, 448)     value bit-plane coefficients, float[16]
 //   [1024, 1280)   Rademacher sign words, 4 roles x 64 bytes (coordinate i of a
 //                  role is bit i % 32 of uint32 word i / 32; 1 means -1)
-//   [2048, ...)    dense variant: Pi_K, G, Pi_V as float[d*d] row-major each
+//   [2048, ...)    dense variant: Pi_K, G, Pi_V as float[d*d] row-major each,
+//                  then for each of them (same order) fp16 hi and lo copies,
+//                  row-major [d][d] each, of s*M with s = 1024 for Pi_K and
+//                  Pi_V and 256 for G: hi = fp16(s M), lo = fp16(s M - hi), the
+//                  operands of the matrix-core append (the scales keep every lo
+//                  piece that matters out of the fp16 subnormal range)
 //
 // Bit-plane coefficients: a symmetric (odd) codebook c over b-bit codes is a
 // multilinear function of the signs s_k = 1 - 2*bit_k(idx):
@@ -54,8 +59,11 @@ struct ParamsHeader {
 static_assert(sizeof(ParamsHeader) == 64, "header is 64 bytes");
 
 inline size_t params_bytes(int d, int rotation) {
-  return kOffDense + (rotation == TQ_ROT_DENSE ? size_t(3) * d * d * sizeof(float) : 0);
+  return kOffDense + (rotation == TQ_ROT_DENSE ? size_t(3) * d * d * (sizeof(float) + 2 * sizeof(uint16_t)) : 0);
 }
+// byte offset of the fp16 split of dense matrix m (0 Pi_K, 1 G, 2 Pi_V); lo follows hi
+constexpr size_t dense16_offset(int d, int m) { return kOffDense + size_t(3) * d * d * 4 + size_t(m) * d * d * 4; }
+constexpr float kDense16Scale[3] = {1024.f, 256.f, 1024.f};
 inline size_t key_block_bytes(int d, int key_bits, int P) { return size_t(key_bits) * P * d / 8 + 8 * size_t(P); }
 inline size_t value_block_bytes(int d, int value_bits, int P) { return size_t(value_bits) * P * d / 8 + 4 * size_t(P); }
 

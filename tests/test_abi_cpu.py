@@ -67,10 +67,16 @@ def test_host_params_match_oracle(d, kb, vb, rot):
             bits = (w[r][np.arange(d) // 32] >> (np.arange(d) % 32).astype(np.uint32)) & 1
             assert np.array_equal(np.where(bits == 1, -1.0, 1.0), arr)
     else:
-        M = f[512:].reshape(3, d, d)
+        M = f[512:512 + 3 * d * d].reshape(3, d, d)
         assert np.abs(M[0] - T.pk).max() < 1e-6
         assert np.abs(M[1] - T.g).max() < 1e-5
         assert np.abs(M[2] - T.pv).max() < 1e-6
+        # fp16 hi/lo operands of the matrix-core append: hi + lo = s M to fp32 precision
+        h16 = blob[2048 + 12 * d * d:2048 + 24 * d * d].view(np.float16).reshape(3, 2, d, d).astype(np.float64)
+        for m, s in enumerate((1024.0, 256.0, 1024.0)):
+            ref = s * M[m].astype(np.float64)
+            assert np.array_equal(h16[m, 0], ref.astype(np.float16).astype(np.float64))
+            assert np.abs(h16[m, 0] + h16[m, 1] - ref).max() <= 2.0 ** -20 * np.abs(ref).max()
 
 
 def test_size_queries_match_layout():
@@ -79,7 +85,7 @@ def test_size_queries_match_layout():
         cfg = tqa.Config(d, 8, 2, kb, vb, 16, 128, rot, 1)
         assert tqa.key_block_bytes(cfg) == layout.key_block_bytes(d, kb)
         assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(d, vb)
-        assert tqa.params_bytes(cfg) == 2048 + (3 * d * d * 4 if rot == "dense" else 0)
+        assert tqa.params_bytes(cfg) == 2048 + (3 * d * d * 8 if rot == "dense" else 0)
         ws = tqa.decode_workspace_bytes(cfg, 3, 1000)
         # at least one partial record (max, denominator, d sums) per (sequence, query head)
         # for the compressed part and one for the window, in float32

@@ -28,11 +28,19 @@ CASES = {
     # shapes outside the matrix-core kernel (head_dim 64, GQA group of 8) use the plain kernels
     "plain_hd64_gqa8": ([300, 130], 2),
     "plain_hd128_gqa8": ([200, 50], 1),
+    # dense rotation, appends of a few tokens per call (partial matrix-core tiles)
+    "dense_short_appends": ([40, 13], 8),
+    # dense rotation at head_dim 64 (the wavefront-per-token kernel)
+    "dense_hd64": ([100, 37], 3),
 }
 
 import workloads as _w
 _w.WORKLOADS.setdefault("plain_hd64_gqa8", _w.GQA_DECODE.replace(
     name="plain_hd64_gqa8", num_q_heads=16, num_kv_heads=2, head_dim=64, key_bits=3, value_bits=3, window=32))
+_w.WORKLOADS.setdefault("dense_hd64", _w.GQA_DECODE.replace(
+    name="dense_hd64", num_q_heads=8, num_kv_heads=2, head_dim=64, key_bits=3, value_bits=2, window=32,
+    rotation="dense"))
+_w.WORKLOADS.setdefault("dense_short_appends", _w.HD256_DENSE_32.replace(name="dense_short_appends", window=16))
 _w.WORKLOADS.setdefault("plain_hd128_gqa8", _w.GQA_DECODE.replace(
     name="plain_hd128_gqa8", num_q_heads=16, num_kv_heads=2, key_bits=4, value_bits=2, window=48,
     rotation="dense"))

@@ -105,6 +105,12 @@ HD256_FWHT_32 = _register(HD256_DENSE_32.replace(
     description="batch 8, 16 q / 4 KV heads, d=256, 32768 ctx, bf16 N(0,1); 3/2-bit; FWHT rotation (comparison arm)",
     rotation="fwht"))
 
+HD256_DENSE_PREFILL = _register(HD256_DENSE_32.replace(
+    name="hd256_dense_prefill",
+    description="the head_dim=256 dense 3/2-bit cache written by one append (8 seqs x 32768 tokens, 4 KV heads), "
+                "then decoded; the dense rotation's matrix-core workload",
+    prefill_seqs=8, prefill_tokens=32768))
+
 OUTLIER_STRESS = _register(Workload(
     name="outlier_stress",
     description="batch 4, 32 q / 8 KV heads, d=128, 131072 ctx; K bf16 N(0,1) with 4 fixed channels per head x20; V Student-t(3); 4/4-bit; FWHT",
