@@ -596,9 +596,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   constexpr int KW = (MK + 1) * KH;    // key words per lane per page
   constexpr int VW = (CBW / 2) * BV;   // value words per lane per page pair
 #ifndef TQ_PAGE_FENCE
-#define TQ_PAGE_FENCE 1
+#define TQ_PAGE_FENCE 0
 #endif
-  constexpr bool kPageFence = TQ_PAGE_FENCE;
+  // scheduling fences between page pairs of the scores: off by default (the
+  // compiler interleaves more pages across the chained MFMAs), kept where the
+  // extra pages in flight would spill (d = 256, 3 key MSE bits, 2 value bits)
+  constexpr bool kPageFence = TQ_PAGE_FENCE || (D == 256 && MK == 3 && BV == 2);
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
