@@ -72,7 +72,7 @@ template <int BITS>
 __device__ __forceinline__ void value_operands(const uint32_t (&w)[4], v8i (&op)[num_planes(BITS)]) {
   v4i f[BITS];
 #pragma unroll
-  for (int b = 0; b < BITS; ++b) f[b] = bits_to_fp4_pm1_dwords(w[b]);
+  for (int b = 0; b < BITS; ++b) f[b] = bits_to_fp4_pm6_dwords(w[b]);
 #pragma unroll
   for (int p = 0; p < num_planes(BITS); ++p) {
     const int sub = odd_subset(BITS, p);
@@ -80,7 +80,7 @@ __device__ __forceinline__ void value_operands(const uint32_t (&w)[4], v8i (&op)
       op[p] = fp4_operand(f[__builtin_ctz(sub)]);
     } else {
       const int b0 = __builtin_ctz(sub), b1 = __builtin_ctz(sub & (sub - 1)), b2 = 31 - __builtin_clz(sub);
-      op[p] = fp4_operand(fp4_pm1_product3(f[b0], f[b1], f[b2]));
+      op[p] = fp4_operand(fp4_pm6_product3(f[b0], f[b1], f[b2]));
     }
   }
 }
@@ -555,20 +555,23 @@ __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
 __host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds) {
   return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds) <= kRegBudget;
 }
-// Wavefronts resident per SIMD.  With at most two value bits at d = 128 the
-// work of a block divides over four wavefronts that each fit in 128
-// registers, so four of them share a SIMD and hide each other's latencies;
-// the other variants need up to 256 registers and run two per SIMD.
-#ifndef TQ_SPLIT_OCC4
-#define TQ_SPLIT_OCC4 0
+// Wavefronts resident per SIMD.  With three or four value bits at d = 128 the
+// work of a block divides over four wavefronts that each fit in 168 registers
+// (query operands read from LDS), so three share a SIMD and hide each other's
+// latencies.  The other variants need up to 256 registers and run two per
+// SIMD: at d = 128 with at most two value bits one wavefront per work item
+// measured faster than four at four per SIMD, whose recent-token window then
+// runs on one of the four.
+#ifndef TQ_SPLIT_OCC3
+#define TQ_SPLIT_OCC3 1
 #endif
 __host__ __device__ constexpr int split_occupancy(int D, int MK, int BV) {
-  return TQ_SPLIT_OCC4 && D == 128 && BV <= 2 ? 4 : 2;
+  return TQ_SPLIT_OCC3 && D == 128 && BV > 2 ? 3 : 2;
 }
 // Variants where the estimate above is too optimistic (the compiled loop
 // spills at the estimated count) and the wavefront count that compiles clean.
 __host__ __device__ constexpr int split_waves_override(int D, int MK, int BV) {
-  return split_occupancy(D, MK, BV) == 4 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
+  return split_occupancy(D, MK, BV) > 2 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
 }
 // wavefronts per work item: the fewest whose registers fit two wavefronts per SIMD
 __host__ __device__ constexpr int split_waves(int D, int MK, int BV) {
@@ -577,7 +580,7 @@ __host__ __device__ constexpr int split_waves(int D, int MK, int BV) {
 }
 // query operands stay in registers when they fit, else each MFMA reads them from LDS
 __host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV) {
-  return split_occupancy(D, MK, BV) == 4 ? false : !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
+  return split_occupancy(D, MK, BV) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
 }
 
 // Re-base a head's reference maximum only when a block's maximum exceeds it by
@@ -602,6 +605,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   // compiler interleaves more pages across the chained MFMAs), kept where the
   // extra pages in flight would spill (d = 256, 3 key MSE bits, 2 value bits)
   constexpr bool kPageFence = TQ_PAGE_FENCE || (D == 256 && MK == 3 && BV == 2);
+#ifndef TQ_PLANE_OUTER
+#define TQ_PLANE_OUTER 1
+#endif
+  constexpr bool kPlaneOuter = TQ_PLANE_OUTER && QL;
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
@@ -780,21 +787,47 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 #pragma unroll
     for (int j = 0; j < PPW; ++j) kok[j] = kid[j] >= 0;
     float loc_max = -INFINITY, loc_vmax = 0.f;
+    // plane products x pages: with the query operands in LDS, each operand is
+    // read once per block and feeds one independent MFMA per page; with them
+    // in registers, page by page (pages interleave across the chains)
+    v4f dm[PPW], dq[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      v4f dm = {k_m, 0.f, 0.f, 0.f}, dq = {k_q, 0.f, 0.f, 0.f};
+      dm[j] = v4f{k_m, 0.f, 0.f, 0.f};
+      dq[j] = v4f{k_q, 0.f, 0.f, 0.f};
+    }
+    if constexpr (kPlaneOuter) {
 #pragma unroll
-      for (int hf = 0; hf < KH; ++hf) {
-        const uint32_t* w = kw[j] + hf * (MK + 1);
+      for (int hf = 0; hf < KH; ++hf)
 #pragma unroll
-        for (int pl = 0; pl < KP; ++pl)
-          dm = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm, sa);
-        dq = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq, sa);
+        for (int pl = 0; pl <= KP; ++pl) {
+          const v8i qo = qop(pl, hf);
+#pragma unroll
+          for (int j = 0; j < PPW; ++j) {
+            const uint32_t* w = kw[j] + hf * (MK + 1);
+            if (pl < KP)
+              dm[j] = mfma_f8_f4(qo, bits_to_fp4_affine(plane_word<MK>(w, pl)), dm[j], sa);
+            else
+              dq[j] = mfma_f8_f4(qo, bits_to_fp4_affine(w[MK]), dq[j], sa);
+          }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      if constexpr (!kPlaneOuter) {
+#pragma unroll
+        for (int hf = 0; hf < KH; ++hf) {
+          const uint32_t* w = kw[j] + hf * (MK + 1);
+#pragma unroll
+          for (int pl = 0; pl < KP; ++pl)
+            dm[j] = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm[j], sa);
+          dq[j] = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq[j], sa);
+        }
       }
       const int pos = tb + (wvu * PPW + j) * kPage + r16;
       // dm[i], dq[i]: part i of head g4 for token r16, already in logit units
-      const float msum = (dm[0] + dm[1]) + (dm[2] + dm[3]);
-      const float qsum = (dq[0] + dq[1]) + (dq[2] + dq[3]);
+      const float msum = (dm[j][0] + dm[j][1]) + (dm[j][2] + dm[j][3]);
+      const float qsum = (dq[j][0] + dq[j][1]) + (dq[j][2] + dq[j][3]);
       const float est = kn[j].x * fmaf(kn[j].y, qsum, msum);
       const bool tok_ok = pos < t_end && kok[j];
       const bool valid = tok_ok && head_ok;
@@ -802,7 +835,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       vnu[j] = tok_ok ? vn[j] : 0.f;
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
-      if constexpr (kPageFence) {
+      if constexpr (kPageFence && !kPlaneOuter) {
         if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the pages in flight
       }
     }
@@ -936,7 +969,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   float* wsh = ws + ((size_t(s) * a.num_q_heads + hk * G + ch) * nrec + split) * rec + 2;
   float cvals[VP];
 #pragma unroll
-  for (int p = 0; p < VP; ++p) cvals[p] = coef_v[odd_subset(BV, p)];
+  for (int p = 0; p < VP; ++p) cvals[p] = coef_v[odd_subset(BV, p)] * (1.f / kPm6);  // planes read +-6
 #pragma unroll
   for (int c = 0; c < CBW; ++c)
 #pragma unroll

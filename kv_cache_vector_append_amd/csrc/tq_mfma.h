@@ -11,7 +11,7 @@
 //    the QJL bits are +-1 already.  Key bits turn into fp4 operands with one
 //    ALU operation per 8 values through an affine encoding
 //    (bits_to_fp4_affine); value bits, whose products are summed over many
-//    tokens, keep the centred +-1 encoding (bits_to_fp4_pm1): an affine
+//    tokens, keep a centred encoding, +-6 (bits_to_fp4_pm6_dwords): an affine
 //    offset there grows with the token count while the result does not, and
 //    costs accuracy in the matrix-core sums.
 //  * The fp32 operand (rotated query, softmax weight) is split into four fp8
@@ -79,17 +79,19 @@ __device__ __forceinline__ v8i bits_to_fp4_affine(uint32_t w) {
 constexpr int kAndOr = 0xEA;  // (a & b) | c
 constexpr int kXor3 = 0x96;   // a ^ b ^ c
 
-// 32 sign bits -> 32 fp4 values +-1 (bit set -> -1.0), same element order as
-// bits_to_fp4_affine: dword j = ((w << (3 - j)) & 0x88888888) | 0x22222222.
-__device__ __forceinline__ v4i bits_to_fp4_pm1_dwords(uint32_t w) {
-  return v4i{int(__builtin_amdgcn_bitop3_b32(w << 3, 0x88888888u, 0x22222222u, kAndOr)),
-             int(__builtin_amdgcn_bitop3_b32(w << 2, 0x88888888u, 0x22222222u, kAndOr)),
-             int(__builtin_amdgcn_bitop3_b32(w << 1, 0x88888888u, 0x22222222u, kAndOr)),
-             int(__builtin_amdgcn_bitop3_b32(w, 0x88888888u, 0x22222222u, kAndOr))};
+// 32 sign bits -> 32 fp4 values +-6 (bit set -> -6.0), same element order as
+// bits_to_fp4_affine, one shift-or per dword: dword j = (w << (3 - j)) |
+// 0x77777777.  The OR forces both exponent bits and the mantissa bit of every
+// nibble to one (e2m1 0111 = 6.0), so whatever bits the shift brings into
+// those places, only the sign bit -- bit 4n + j of w -- carries data.
+constexpr uint32_t kPm6Fill = 0x77777777u;
+constexpr float kPm6 = 6.f;
+__device__ __forceinline__ v4i bits_to_fp4_pm6_dwords(uint32_t w) {
+  return v4i{int((w << 3) | kPm6Fill), int((w << 2) | kPm6Fill), int((w << 1) | kPm6Fill), int(w | kPm6Fill)};
 }
-// The +-1 encoding of the XOR of three bit words: XOR of their encodings (the
-// 1.0 magnitude bits of three operands XOR back to 1.0, the signs multiply).
-__device__ __forceinline__ v4i fp4_pm1_product3(const v4i& a, const v4i& b, const v4i& c) {
+// The +-6 encoding of the XOR of three bit words: XOR of their encodings (the
+// 0111 magnitude bits of three operands XOR back to 0111, the signs multiply).
+__device__ __forceinline__ v4i fp4_pm6_product3(const v4i& a, const v4i& b, const v4i& c) {
   return v4i{int(__builtin_amdgcn_bitop3_b32(uint32_t(a[0]), uint32_t(b[0]), uint32_t(c[0]), kXor3)),
              int(__builtin_amdgcn_bitop3_b32(uint32_t(a[1]), uint32_t(b[1]), uint32_t(c[1]), kXor3)),
              int(__builtin_amdgcn_bitop3_b32(uint32_t(a[2]), uint32_t(b[2]), uint32_t(c[2]), kXor3)),
@@ -99,7 +101,6 @@ __device__ __forceinline__ v4i fp4_pm1_product3(const v4i& a, const v4i& b, cons
 __device__ __forceinline__ v8i fp4_operand(const v4i& lo) {
   return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
 }
-__device__ __forceinline__ v8i bits_to_fp4_pm1(uint32_t w) { return fp4_operand(bits_to_fp4_pm1_dwords(w)); }
 
 // Operand factor f_j for the element group j = (bit position) % 4 of the above.
 __host__ __device__ constexpr float fp4_affine_factor(int j) {
