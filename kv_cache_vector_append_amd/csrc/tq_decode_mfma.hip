@@ -608,7 +608,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 #ifndef TQ_PLANE_OUTER
 #define TQ_PLANE_OUTER 1
 #endif
-  constexpr bool kPlaneOuter = TQ_PLANE_OUTER && QL;
+  constexpr bool kPlaneOuter = TQ_PLANE_OUTER && QL && PPW <= 4;  // eight pages of accumulators would spill
+#ifndef TQ_ROLL_KEYS
+#define TQ_ROLL_KEYS 1
+#endif
+  constexpr bool kRollKeys = TQ_ROLL_KEYS && !kPlaneOuter;  // key pages re-requested one by one
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
@@ -734,21 +738,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   float2 kn[PPW];
   float vn[PPW];
   uint32_t vw[2][VW];  // value words of the block
+  auto load_key_page = [&](int j) {
+    kid[j] = checked(nkid[j]);
+    const int ph = max(kid[j], 0);
+    const uint8_t* kb = kbase + size_t(ph) * kstride;
+    const uint8_t* vb = vbase + size_t(ph) * vstride;
+    // uniform base + 32-bit lane offset, kept inside the loop so that the
+    // loads take the scalar-base addressing form (no 64-bit vector adds)
+    uint32_t ko = k_off, kno = kn_off, vno = vn_off;
+    asm volatile("" : "+v"(ko), "+v"(kno), "+v"(vno));
+    load_words<KW>(kb + ko, kw[j]);
+    kn[j] = *reinterpret_cast<const float2*>(kb + kno);
+    vn[j] = *reinterpret_cast<const float*>(vb + vno);
+  };
   auto load_keys = [&]() {
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      kid[j] = checked(nkid[j]);
-      const int ph = max(kid[j], 0);
-      const uint8_t* kb = kbase + size_t(ph) * kstride;
-      const uint8_t* vb = vbase + size_t(ph) * vstride;
-      // uniform base + 32-bit lane offset, kept inside the loop so that the
-      // loads take the scalar-base addressing form (no 64-bit vector adds)
-      uint32_t ko = k_off, kno = kn_off, vno = vn_off;
-      asm volatile("" : "+v"(ko), "+v"(kno), "+v"(vno));
-      load_words<KW>(kb + ko, kw[j]);
-      kn[j] = *reinterpret_cast<const float2*>(kb + kno);
-      vn[j] = *reinterpret_cast<const float*>(vb + vno);
-    }
+    for (int j = 0; j < PPW; ++j) load_key_page(j);
   };
   auto load_values = [&]() {
     // lane group g4 reads pages 2 g4 and 2 g4 + 1 of the block
@@ -814,6 +819,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     }
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
+      float2 knj = kn[j];
+      float vnj = vn[j];
       if constexpr (!kPlaneOuter) {
 #pragma unroll
         for (int hf = 0; hf < KH; ++hf) {
@@ -823,16 +830,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
             dm[j] = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm[j], sa);
           dq[j] = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq[j], sa);
         }
+        // this page's registers are consumed: request the next block's page
+        // now, so that the wavefront's key requests stay spread over the
+        // block instead of leaving in one burst
+        if constexpr (kRollKeys) load_key_page(j);
       }
       const int pos = tb + (wvu * PPW + j) * kPage + r16;
       // dm[i], dq[i]: part i of head g4 for token r16, already in logit units
       const float msum = (dm[j][0] + dm[j][1]) + (dm[j][2] + dm[j][3]);
       const float qsum = (dq[j][0] + dq[j][1]) + (dq[j][2] + dq[j][3]);
-      const float est = kn[j].x * fmaf(kn[j].y, qsum, msum);
+      const float est = knj.x * fmaf(knj.y, qsum, msum);
       const bool tok_ok = pos < t_end && kok[j];
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? est : -INFINITY;
-      vnu[j] = tok_ok ? vn[j] : 0.f;
+      vnu[j] = tok_ok ? vnj : 0.f;
       loc_max = fmaxf(loc_max, sc[j]);
       loc_vmax = fmaxf(loc_vmax, vnu[j]);
       if constexpr (kPageFence && !kPlaneOuter) {
@@ -846,7 +857,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
         if (sc[j] != -INFINITY) a.logits[(size_t(s) * a.num_q_heads + hk * G + g4) * a.max_ctx + pos] = sc[j] * kLn2;
       }
     }
-    load_keys();
+    if constexpr (!kRollKeys) load_keys();
     // ---------------------------------------------- block maximum, weight range
     loc_max = max16(loc_max);
     loc_vmax = max16(loc_vmax);
