@@ -423,8 +423,12 @@ __device__ __forceinline__ float centroid_mag(const float* cu, const float (&d)[
   }
 }
 
+// Two wavefronts per SIMD: the kernel is bound by its ALU work, and a second
+// wavefront hides the latencies of the butterfly chains; at d = 128 the
+// register budget of 256 costs a few spilled words around the phases (measured
+// faster than one wavefront per SIMD with every value in registers).
 template <int D, int MK, int BV>
-__global__ __launch_bounds__(64) void append_tok_kernel(AppendArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void append_tok_kernel(AppendArgs a) {
   constexpr int P = 16, NG = D / 32;
   // upper thresholds and centroids of the odd codebooks (at least one entry)
   constexpr int NKT = (1 << (MK - 1)) - 1 > 0 ? (1 << (MK - 1)) - 1 : 1, NKC = 1 << (MK - 1);
