@@ -315,17 +315,20 @@ __device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t s) {
 // hoisted over a long computation would hold its registers throughout).
 __device__ __forceinline__ void phase() { __builtin_amdgcn_sched_barrier(0); }
 
-// x <- D x, with D as a table of +-1.0 in LDS (read as broadcasts)
+// x <- D x for the sign vector of one role: bit c % 32 of word c / 32 set
+// means -1.  The words are uniform (scalar loads), so each coordinate's sign
+// mask is formed on the scalar unit and applied with one XOR of the float's
+// sign bit -- bit for bit the product with -1.0 or +1.0, with no table and no
+// registers held for it.
 template <int N>
-__device__ __forceinline__ void flip_signs(float (&x)[N], const float* sgn) {
+__device__ __forceinline__ void flip_signs(float (&x)[N], const const_u32* sw) {
+  uint32_t w[N / 32];
 #pragma unroll
-  for (int c = 0; c < N; c += 4) {
-    const float4 s4 = *reinterpret_cast<const float4*>(sgn + c);
-    x[c] *= s4.x;
-    x[c + 1] *= s4.y;
-    x[c + 2] *= s4.z;
-    x[c + 3] *= s4.w;
-    if ((c & 31) == 28) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight
+  for (int q = 0; q < N / 32; ++q) w[q] = sw[q];
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const uint32_t m = (w[c >> 5] << (31 - (c & 31))) & 0x80000000u;
+    x[c] = __uint_as_float(__float_as_uint(x[c]) ^ m);
   }
 }
 
@@ -424,9 +427,8 @@ __device__ __forceinline__ float centroid_mag(const float* cu, const float (&d)[
 }
 
 // Two wavefronts per SIMD: the kernel is bound by its ALU work, and a second
-// wavefront hides the latencies of the butterfly chains; at d = 128 the
-// register budget of 256 costs a few spilled words around the phases (measured
-// faster than one wavefront per SIMD with every value in registers).
+// wavefront hides the latencies of the butterfly chains (a head vector of
+// d = 128 floats per lane fits in the 256 registers each then has).
 template <int D, int MK, int BV>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void append_tok_kernel(AppendArgs a) {
   constexpr int P = 16, NG = D / 32;
@@ -474,19 +476,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   const size_t row = (size_t(b0) + (pos - start)) * H + h;
 
   const const_f32* prm = (const const_f32*)a.params;
-  // the four sign vectors (roles KR, KS1, KS2, VR) as +-1.0 tables
-  __shared__ __attribute__((aligned(16))) float sgn[4][D];
-  {
-    const uint32_t* sw = reinterpret_cast<const uint32_t*>(a.params + kOffSigns);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = lane; c < D; c += 64)
-        sgn[r][c] = ((sw[r * (kSignRoleBytes / 4) + (c >> 5)] >> (c & 31)) & 1u) ? -1.f : 1.f;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // the four sign vectors (roles KR, KS1, KS2, VR), read through the scalar cache
+  const const_u32* sgn_words = (const const_u32*)(a.params + kOffSigns);
+  auto sgn = [&](int role) { return sgn_words + role * (kSignRoleBytes / 4); };
   const float sqd = sqrtf(float(D));
   const size_t plane_bytes = size_t(P) * D / 8;
 
@@ -511,7 +503,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
 #pragma unroll
   for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kscale;
   phase();
-  flip_signs<D>(x, sgn[kRoleKeyRot]);
+  flip_signs<D>(x, sgn(kRoleKeyRot));
   fwht_regs<D>(x);
   phase();
   // codes, residual e = z - c[idx] (in place), its norm
@@ -545,9 +537,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   const float gamma = sqrtf(es) * (zero ? 0.f : 1.f / kscale);
   phase();
   // QJL: z = [S e < 0] with S = H D2 H_n D1 (the positive factors drop out)
-  flip_signs<D>(x, sgn[kRoleSketch1]);
+  flip_signs<D>(x, sgn(kRoleSketch1));
   fwht_regs<D>(x);
-  flip_signs<D>(x, sgn[kRoleSketch2]);
+  flip_signs<D>(x, sgn(kRoleSketch2));
   fwht_regs<D>(x);
   phase();
 #pragma unroll
@@ -606,7 +598,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
 #pragma unroll
   for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * vscale;
   phase();
-  flip_signs<D>(x, sgn[kRoleValueRot]);
+  flip_signs<D>(x, sgn(kRoleValueRot));
   fwht_regs<D>(x);
   phase();
   // plane masks of coordinate pairs, gathered at the lane of the pair:
