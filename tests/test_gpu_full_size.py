@@ -1,0 +1,242 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration bench.py
+times.
+
+The caches are filled by bench.py's own setup functions (same appends, same
+decode split plan); the seeded device generator is then replayed to recover
+the inputs at sampled positions.  The oracle cannot redo these sizes whole, so
+it checks what it can compute piece by piece:
+
+  * append: sampled token-heads (first and last positions, page edges, the
+    window boundary, random positions) re-encoded by the oracle from their
+    inputs: codes and QJL bits bit-exact up to the threshold band, norms at
+    NORM_RTOL;
+  * decode: for one kv head of one sequence, the oracle decodes the GPU's own
+    bytes of every token of that head (a cache holding that head alone) and
+    the GPU's output for the head's query group must agree within DECODE_TOL;
+    the logits the kernel dumps are checked at sampled positions of every
+    query head against the oracle's estimate from the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import workloads
+from harness import BAND, DECODE_TOL, NORM_RTOL, _near_threshold, decode_error
+from oracle import tq
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _ocfg(w, num_q_heads=None, num_kv_heads=None):
+    return tq.Config(w.head_dim, num_q_heads or w.num_q_heads, num_kv_heads or w.num_kv_heads, w.key_bits,
+                     w.value_bits, w.page_tokens, w.window, w.rotation, w.method_seed)
+
+
+def _sample_positions(w, L, rng, extra=24):
+    P, W = w.page_tokens, w.window
+    pos = {0, 1, P - 1, P, L - 1, L - 2}
+    if W:
+        pos |= {max(0, L - W - 1), max(0, L - W), L - W + 1}
+    pos |= set(int(x) for x in rng.integers(0, L, extra))
+    return np.array(sorted(p for p in pos if 0 <= p < L), dtype=np.int64)
+
+
+def _gpu_blocks(cache, bt_row, positions, page):
+    """Key and value blocks of the pages holding `positions`, as an oracle cache
+    over just those pages (block table remapped)."""
+    pages = np.unique(bt_row[positions // page])
+    kb = cache.k_pages[torch.from_numpy(pages).to(DEV)].cpu().numpy()
+    vb = cache.v_pages[torch.from_numpy(pages).to(DEV)].cpu().numpy()
+    return pages, kb, vb
+
+
+def _check_append(w, P, cache, bt, samples, inputs):
+    """samples: {slot: positions}; inputs: {slot: (k rows, v rows)} float64 [n, H, d]."""
+    d, H = w.head_dim, w.num_kv_heads
+    cfg = _ocfg(w)
+    flips = 0
+    for slot, pos in samples.items():
+        pages, kb, vb = _gpu_blocks(cache, bt[slot], pos, w.page_tokens)
+        remap = {int(p): i for i, p in enumerate(pages)}
+        c = tq.Cache(cfg, len(pages), np.zeros((1, 1), np.int64))
+        c.load_bytes(kb, vb)
+        pg = np.array([remap[int(p)] for p in bt[slot][pos // w.page_tokens]])
+        t = pos % w.page_tokens
+        kx, vx = inputs[slot]
+        ek = tq.encode_keys(P, kx.reshape(-1, d))
+        ev = tq.encode_values(P, vx.reshape(-1, d))
+        gk = c.k_codes[pg, :, t].reshape(-1, d).astype(np.int64)
+        gz = c.k_z[pg, :, t].reshape(-1, d)
+        mism = gk != ek["codes"]
+        near = _near_threshold(ek["y"], P.kt)
+        assert not (mism & ~near).any(), f"slot {slot}: key codes differ away from a threshold"
+        flips += int(mism.sum())
+        e = ek["y"] - P.kc[gk]
+        wv = np.where(mism.any(axis=1)[:, None], P.T.sketch(e), ek["w"])
+        zexp = wv < 0
+        zexp[ek["nu"] == 0] = False
+        zm = gz != zexp
+        assert not (zm & ~(np.abs(wv) / np.sqrt(d) < BAND)).any(), f"slot {slot}: QJL bits differ"
+        gnu = c.k_nu[pg, :, t].reshape(-1).astype(np.float64)
+        ggam = c.k_gamma[pg, :, t].reshape(-1).astype(np.float64)
+        ogam = np.where(ek["nu"] == 0, 0.0, np.linalg.norm(e, axis=1))
+        assert np.all(np.abs(gnu - ek["nu"]) <= NORM_RTOL * np.maximum(ek["nu"], 1e-30))
+        assert np.all(np.abs(ggam - ogam) <= NORM_RTOL * np.maximum(ogam, 1e-30))
+        gv = c.v_codes[pg, :, t].reshape(-1, d).astype(np.int64)
+        vm = gv != ev["codes"]
+        assert not (vm & ~_near_threshold(ev["y"], P.vt)).any(), f"slot {slot}: value codes differ"
+        flips += int(vm.sum())
+        gvn = c.v_nu[pg, :, t].reshape(-1).astype(np.float64)
+        assert np.all(np.abs(gvn - ev["nu"]) <= NORM_RTOL * np.maximum(ev["nu"], 1e-30))
+    return flips
+
+
+def _check_decode_head(w, cache, bt, slot, hk, L, q, out_gpu):
+    """Oracle decode of one kv head of one sequence over the GPU's bytes of that
+    head, against the GPU output of the head's query group."""
+    G, d, W = w.gqa, w.head_dim, w.window
+    cfg1 = _ocfg(w, num_q_heads=G, num_kv_heads=1)
+    P1 = tq.Params(cfg1)
+    npg = -(-L // w.page_tokens)
+    pages = torch.from_numpy(bt[slot][:npg].astype(np.int64)).to(DEV)
+    kb = cache.k_pages[pages, hk:hk + 1].cpu().numpy()
+    vb = cache.v_pages[pages, hk:hk + 1].cpu().numpy()
+    c = tq.Cache(cfg1, npg, np.arange(npg, dtype=np.int64)[None])
+    kwin = vwin = None
+    if W:
+        kwin = cache.k_window[slot, hk:hk + 1].cpu().numpy().view(np.float16)[None]
+        vwin = cache.v_window[slot, hk:hk + 1].cpu().numpy().view(np.float16)[None]
+    c.load_bytes(kb, vb, kwin, vwin)
+    qg = q[slot, hk * G:(hk + 1) * G].double().cpu().numpy()[None]
+    ref, lg = tq.decode(P1, c, qg, [0], [L], return_logits=True)
+    return decode_error(out_gpu[slot, hk * G:(hk + 1) * G][None], ref), lg[0]
+
+
+def _decode(S, cache, logits=None):
+    import kv_cache_vector_append_amd as tqa
+    tqa.decode_attention(S.cfg, S.params, cache, S.q, S.dec_slots, S.dec_lens, S.max_ctx, S.out, S.ws,
+                         0.0, logits)
+    torch.cuda.synchronize()
+    return S.out.cpu().double().numpy()
+
+
+def _logit_samples(w, S, cache, bt, slot, rng):
+    """Dumped logits at sampled positions of every query head of `slot`, against
+    the oracle's estimate from the same bytes (window positions: q . k / sqrt(d))."""
+    L, d, H, G = S.lens[slot], w.head_dim, w.num_kv_heads, w.gqa
+    logits = torch.full((len(S.lens), w.num_q_heads, S.max_ctx), float("nan"), device=DEV)
+    _decode(S, cache, logits)
+    lg = logits[slot].cpu().double().numpy()
+    pos = _sample_positions(w, L, rng, extra=64)
+    nc = tq.compressed_count(_ocfg(w), L)
+    pos_c = pos[pos < nc]
+    pages, kb, vb = _gpu_blocks(cache, bt[slot], pos_c, w.page_tokens)
+    remap = {int(p): i for i, p in enumerate(pages)}
+    c = tq.Cache(_ocfg(w), len(pages), np.zeros((1, 1), np.int64))
+    c.load_bytes(kb, vb)
+    pg = np.array([remap[int(p)] for p in bt[slot][pos_c // w.page_tokens]])
+    t = pos_c % w.page_tokens
+    P = tq.Params(_ocfg(w))
+    q = S.q[slot].double().cpu().numpy()
+    worst = 0.0
+    for g in range(H):
+        est = tq.estimate_scores(P, q[g * G:(g + 1) * G], c.k_codes[pg, g, t], c.k_z[pg, g, t], c.k_nu[pg, g, t],
+                                 c.k_gamma[pg, g, t]) / np.sqrt(d)
+        got = lg[g * G:(g + 1) * G][:, pos_c]
+        scale = np.abs(est).max()
+        worst = max(worst, float(np.abs(got - est).max() / scale))
+    assert worst <= 1e-4, worst
+    return worst
+
+
+def test_full_size_outlier_stress_decode():
+    """4 x 131072 tokens, 32 q / 8 KV heads, 4/4-bit, FWHT: the default bench workload."""
+    import kv_cache_vector_append_amd as tqa
+    w = workloads.WORKLOADS["outlier_stress"]
+    torch.cuda.set_device(DEV)
+    S = bench.build_decode_setup(w, tqa, torch, DEV)
+    nseq, ctx = w.decode_seqs, w.decode_ctx
+    # the timed step: append token ctx - 1 of every sequence, decode over ctx tokens
+    tqa.quantize_append(S.cfg, S.params, S.cache, S.step_k, S.step_v, *S.app_args)
+    out = _decode(S, S.cache)
+    assert np.isfinite(out).all()
+    # replay the device generator for the inputs at sampled positions
+    rng = np.random.default_rng(20241)
+    samples = {s: _sample_positions(w, ctx, rng) for s in range(nseq)}
+    inputs = {s: ([], []) for s in range(nseq)}
+    g = workloads.device_generator(w, 1, DEV)
+    chunk = 16384
+    for start in range(0, ctx - 1, chunk):
+        n = min(chunk, ctx - 1 - start)
+        k = workloads.device_kv(w, "k", nseq * n, g, DEV)
+        v = workloads.device_kv(w, "v", nseq * n, g, DEV)
+        for s in range(nseq):
+            sel = samples[s][(samples[s] >= start) & (samples[s] < start + n)]
+            rows = torch.from_numpy(s * n + sel - start).to(DEV)
+            inputs[s][0].append(k[rows].double().cpu().numpy())
+            inputs[s][1].append(v[rows].double().cpu().numpy())
+        del k, v
+    step_k = workloads.device_kv(w, "k", nseq, g, DEV)
+    step_v = workloads.device_kv(w, "v", nseq, g, DEV)
+    q = workloads.device_queries(w, nseq, g, DEV)
+    assert torch.equal(step_k, S.step_k) and torch.equal(q, S.q), "device generator replay diverged"
+    for s in range(nseq):
+        if samples[s][-1] == ctx - 1:
+            inputs[s][0].append(step_k[s:s + 1].double().cpu().numpy())
+            inputs[s][1].append(step_v[s:s + 1].double().cpu().numpy())
+        inputs[s] = (np.concatenate(inputs[s][0]), np.concatenate(inputs[s][1]))
+    bt = S.cache.block_table.cpu().numpy()
+    P = tq.Params(_ocfg(w))
+    flips = _check_append(w, P, S.cache, bt, samples, inputs)
+    err, _ = _check_decode_head(w, S.cache, bt, 2, 5, ctx, S.q, out)
+    worst = _logit_samples(w, S, S.cache, bt, 1, rng)
+    print(f"[full size] outlier_stress: {sum(len(p) for p in samples.values()) * w.num_kv_heads} sampled "
+          f"token-heads ({flips} band flips), decode err {err:.3g} (seq 2, kv head 5, {ctx} tokens), "
+          f"logit rel err {worst:.3g}", flush=True)
+    assert err <= DECODE_TOL
+
+
+def test_full_size_mixed_serving_step():
+    """64 x 4096-token append into shuffled pages, then decode of 256 x 4096."""
+    import kv_cache_vector_append_amd as tqa
+    w = workloads.WORKLOADS["mixed_serving"]
+    torch.cuda.set_device(DEV)
+    S = bench.build_mixed_setup(w, tqa, torch, DEV)
+    nseq, ctx, npre, ntok = w.decode_seqs, w.decode_ctx, w.prefill_seqs, w.prefill_tokens
+    tqa.quantize_append(S.cfg, S.params, S.cache, S.step_k, S.step_v, *S.app_args)
+    out = _decode(S, S.cache)
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(20242)
+    # samples: two prefilled sequences and two of the timed append
+    pick = [npre, nseq - 1, 0, npre - 1]
+    samples = {s: _sample_positions(w, ctx, rng) for s in pick}
+    inputs = {}
+    g = workloads.device_generator(w, 1, DEV)
+    group = 32
+    for s0 in range(npre, nseq, group):
+        ns = min(group, nseq - s0)
+        k = workloads.device_kv(w, "k", ns * ctx, g, DEV)
+        v = workloads.device_kv(w, "v", ns * ctx, g, DEV)
+        for s in pick:
+            if s0 <= s < s0 + ns:
+                rows = torch.from_numpy((s - s0) * ctx + samples[s]).to(DEV)
+                inputs[s] = (k[rows].double().cpu().numpy(), v[rows].double().cpu().numpy())
+        del k, v
+    step_k = workloads.device_kv(w, "k", npre * ntok, g, DEV)
+    step_v = workloads.device_kv(w, "v", npre * ntok, g, DEV)
+    assert torch.equal(step_k, S.step_k), "device generator replay diverged"
+    for s in pick:
+        if s < npre:
+            rows = torch.from_numpy(s * ntok + samples[s]).to(DEV)
+            inputs[s] = (step_k[rows].double().cpu().numpy(), step_v[rows].double().cpu().numpy())
+    bt = S.cache.block_table.cpu().numpy()
+    P = tq.Params(_ocfg(w))
+    flips = _check_append(w, P, S.cache, bt, samples, inputs)
+    errs = [_check_decode_head(w, S.cache, bt, s, hk, ctx, S.q, out)[0] for s, hk in ((3, 0), (200, 7))]
+    worst = _logit_samples(w, S, S.cache, bt, 17, rng)
+    print(f"[full size] mixed_serving: {sum(len(p) for p in samples.values()) * w.num_kv_heads} sampled "
+          f"token-heads ({flips} band flips), decode err {max(errs):.3g}, logit rel err {worst:.3g}", flush=True)
+    assert max(errs) <= DECODE_TOL
