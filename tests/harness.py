@@ -1,7 +1,7 @@
 """Test harness: runs the HIP library and the oracle on the same seeded inputs
 and compares them under the parity rules.
 
-Parity rules (from the acceptance criteria of this build):
+Parity rules:
   * codes and QJL bits are bit-exact, except a code whose pre-quantization
     coordinate lies within 1e-6 of a threshold (counted, reported); for a token
     with such a flip, the QJL bits are re-derived from the GPU's codes, and a
