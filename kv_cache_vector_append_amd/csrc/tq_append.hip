@@ -386,7 +386,7 @@ __device__ __forceinline__ void store_f16_row(uint16_t* dst, const float (&x)[N]
 // thresholds tu = t[L/2 .. L-2], complemented when z < 0 (up to ties, which
 // sit inside any rounding band).  Every decision is kept as the sign bit of a
 // float: bit j of m is the sign of d_j = tu_(...) - |z| (a binary search), the
-// code's top bit is NOT sign(z), and its bit j < M-1 is sign(d_j XOR z).  Bits
+// code's top bit is NOT sign(z), and its bit j < M-1 is sign(d_j) XOR sign(z).  Bits
 // are shifted into words with v_alignbit and selections use masks built from
 // sign bits, so no comparison result has to stay alive as a lane mask.
 __device__ __forceinline__ uint32_t sign_mask(float d) { return uint32_t(int32_t(__float_as_uint(d)) >> 31); }
@@ -520,9 +520,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
       const uint32_t zb = __float_as_uint(z);
       float dm[4];
       magnitude_signs<MK>(fabsf(z), tk, dm);
-      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);  // inverted below
+      // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
+      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
 #pragma unroll
-      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]) ^ zb);
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
       const float e = z - __builtin_copysignf(centroid_mag<MK>(ck, dm), z);
       x[c] = e;
       es = fmaf(e, e, es);
@@ -532,6 +533,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
       for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
       asm volatile("" : "+v"(es));
     }
+#pragma unroll
+    for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
     kw[MK - 1][gg] = ~kw[MK - 1][gg];
   }
   const float gamma = sqrtf(es) * (zero ? 0.f : 1.f / kscale);
@@ -602,8 +605,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   fwht_regs<D>(x);
   phase();
   // plane masks of coordinate pairs, gathered at the lane of the pair:
-  // vm[p][parity][half] holds, at lane i, bits of coordinate 2 i + parity
-  const bool vbit_ok = valid && !vzero;
+  // vm[p][parity][half] holds, at lane i, bits of coordinate 2 i + parity.
+  // Each is a wavefront mask of at most two comparisons: the top bit is NOT
+  // sign(z), bit p below it sign(d_p) XOR sign(z), formed on the masks.
+  // Lanes without a stored token (or with a zero norm) are cleared once at
+  // the end.
+  const uint64_t okm = __ballot(valid && !vzero);
   uint32_t vm[BV][2][2];
 #pragma unroll
   for (int p = 0; p < BV; ++p)
@@ -612,17 +619,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   static_for<0, D>([&](auto ci) {
     constexpr int c = decltype(ci)::value;
     const float z = x[c];
-    const uint32_t zb = __float_as_uint(z);
     float dm[4];
     magnitude_signs<BV>(fabsf(z), tv, dm);
+    const uint64_t neg = __ballot(int32_t(__float_as_uint(z)) < 0);
 #pragma unroll
     for (int p = 0; p < BV; ++p) {
-      const bool bit = p == BV - 1 ? int32_t(zb) >= 0 : int32_t(__float_as_uint(dm[p]) ^ zb) < 0;
-      const uint64_t m = __ballot(bit && vbit_ok);
+      const uint64_t m = p == BV - 1 ? ~neg : __ballot(int32_t(__float_as_uint(dm[p])) < 0) ^ neg;
       vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
       vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
     }
   });
+#pragma unroll
+  for (int p = 0; p < BV; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      vm[p][q][0] &= uint32_t(okm);
+      vm[p][q][1] &= uint32_t(okm >> 32);
+    }
   if (page_ok) *reinterpret_cast<float*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block +
                                          size_t(BV) * plane_bytes + 4 * t) = vzero ? 0.f : vnu;
   // lane i < d/2 stores the words of coordinate pair i in each of the four pages
@@ -931,9 +944,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const uint32_t zb = __float_as_uint(zz);
       float dm[4];
       magnitude_signs<MK>(fabsf(zz), tk, dm);
-      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);  // inverted below
+      // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
+      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
 #pragma unroll
-      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]) ^ zb);
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
       const float e = zz - __builtin_copysignf(centroid_mag<MK>(ck, dm), zz);
       z[c] = e;
       es = fmaf(e, e, es);
@@ -948,6 +962,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         store_pieces(buf + t * DT::ROWB + (q * Q + 32 * gg + c) * 4, v);
       }
     }
+#pragma unroll
+    for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
     kw[MK - 1][gg] = ~kw[MK - 1][gg];
   }
   esum[q][t] = es;
@@ -989,21 +1005,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int p = 0; p < BV; ++p)
 #pragma unroll
     for (int r = 0; r < 2; ++r) vm[p][r][0] = vm[p][r][1] = 0u;
+  // bits as wavefront masks, as in the token-per-lane kernel
+  const uint64_t okm = __ballot(vbit_ok);
   static_for<0, Q>([&](auto ci) {
     constexpr int c = decltype(ci)::value;
     if constexpr (c % 32 == 0) read_group(c / 32);
     const float zz = z[c % 32];
-    const uint32_t zb = __float_as_uint(zz);
     float dm[4];
     magnitude_signs<BV>(fabsf(zz), tv, dm);
+    const uint64_t neg = __ballot(int32_t(__float_as_uint(zz)) < 0);
 #pragma unroll
     for (int p = 0; p < BV; ++p) {
-      const bool bit = p == BV - 1 ? int32_t(zb) >= 0 : int32_t(__float_as_uint(dm[p]) ^ zb) < 0;
-      const uint64_t m = __ballot(bit && vbit_ok);
+      const uint64_t m = p == BV - 1 ? ~neg : __ballot(int32_t(__float_as_uint(dm[p])) < 0) ^ neg;
       vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
       vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
     }
   });
+#pragma unroll
+  for (int p = 0; p < BV; ++p)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      vm[p][r][0] &= uint32_t(okm);
+      vm[p][r][1] &= uint32_t(okm >> 32);
+    }
   if (page_ok && q == 0)
     *reinterpret_cast<float*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block + size_t(BV) * plane_bytes +
                               4 * ts) = vbit_ok ? vnu : 0.f;
