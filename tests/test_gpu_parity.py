@@ -175,3 +175,37 @@ def test_zero_vector_append():
     q = queries(w, 1)
     o_gpu, _ = gpu_decode(run, q, lens=[21])
     assert np.isfinite(o_gpu).all()
+
+
+@pytest.mark.parametrize("value_bits", [2, 4])
+def test_zero_rows_inside_long_appends(monkeypatch, value_bits):
+    """Zero key or value rows inside appends of 100 and 70 tokens, which take the
+    token-per-lane kernel: each zero row stores nu = gamma = 0 and all-zero bits,
+    while its neighbours in the same wavefront keep their codes bit for bit."""
+    zero_rows = {"k": (3, 40, 77), "v": (5, 40, 64)}
+    orig = workloads.kv_tokens
+
+    def with_zero_rows(w, which, seq, start, count):
+        x = orig(w, which, seq, start, count).clone()
+        for r in zero_rows[which]:
+            if start <= r < start + count:
+                x[r - start] = 0
+        return x
+
+    monkeypatch.setattr(workloads, "kv_tokens", with_zero_rows)
+    w = workloads.GQA_DECODE.replace(num_q_heads=8, num_kv_heads=2, window=16, value_bits=value_bits,
+                                     key_bits=4 if value_bits == 4 else 3)
+    run = make_run(w, [100, 70])
+    rep = compare_append(run)
+    assert rep.tokens == 170 * w.num_kv_heads and rep.unexcused == 0 and rep.window_mismatch == 0
+    gc = gpu_cache_as_oracle(run)
+    for s, n in enumerate(run.lens):
+        g = gc.gather(s, [r for r in zero_rows["k"] if r < n])
+        assert not g["k_nu"].any() and not g["k_gamma"].any()
+        assert not g["k_codes"].any() and not g["k_z"].any()
+        g = gc.gather(s, [r for r in zero_rows["v"] if r < n])
+        assert not g["v_nu"].any() and not g["v_codes"].any()
+    q = queries(w, 2)
+    o_gpu, _ = gpu_decode(run, q)
+    o_ref = tq.decode(run.P, gc, q.double().numpy(), np.arange(2), run.lens)
+    assert decode_error(o_gpu, o_ref) <= DECODE_TOL
