@@ -311,6 +311,23 @@ __device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t s) {
   return v;
 }
 
+// One exchange step of a 16 x 16 bit transpose over the 16 lanes of a row,
+// done on both 16-bit halves of the word at once.  Lane l swaps, with lane
+// l ^ S, the bits c of its half-words with (c & S) != (l & S): the lane with
+// bit S clear keeps the bits with (c & S) == 0 and takes the partner's other
+// bits moved down by S (a rotation), the other lane the converse.  Steps 8, 4,
+// 2 and 1 together move bit c of lane l to bit l of lane c.
+template <int S>
+__device__ __forceinline__ uint32_t transpose16_step(uint32_t a, int lane) {
+  constexpr uint32_t kHi = S == 8 ? 0xff00ff00u : S == 4 ? 0xf0f0f0f0u : S == 2 ? 0xccccccccu : 0xaaaaaaaau;
+  // ds_swizzle in bit mode: partner = lane ^ S within each 32-lane half
+  const uint32_t p = uint32_t(__builtin_amdgcn_ds_swizzle(int(a), 0x1f | (S << 10)));
+  const bool hi = (lane & S) != 0;
+  const uint32_t r = __builtin_amdgcn_alignbit(p, p, hi ? S : 32 - S);  // rotate right
+  const uint32_t keep = hi ? kHi : ~kHi;
+  return (a & keep) | (r & ~keep);
+}
+
 // Keeps the scheduler from moving work across phases (loads of the next phase
 // hoisted over a long computation would hold its registers throughout).
 __device__ __forceinline__ void phase() { __builtin_amdgcn_sched_barrier(0); }
@@ -604,57 +621,63 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   flip_signs<D>(x, sgn(kRoleValueRot));
   fwht_regs<D>(x);
   phase();
-  // plane masks of coordinate pairs, gathered at the lane of the pair:
-  // vm[p][parity][half] holds, at lane i, bits of coordinate 2 i + parity.
-  // Each is a wavefront mask of at most two comparisons: the top bit is NOT
-  // sign(z), bit p below it sign(d_p) XOR sign(z), formed on the masks.
-  // Lanes without a stored token (or with a zero norm) are cleared once at
-  // the end.
-  const uint64_t okm = __ballot(valid && !vzero);
-  uint32_t vm[BV][2][2];
+  // Value bits in the page layout (per coordinate pair, the 16 token bits of
+  // each coordinate) without ballots.  Each lane packs its own token's bits
+  // of a 32-coordinate group into one word per plane, even coordinates in the
+  // low half and odd ones in the high half: bit k of a half is coordinate pair
+  // k.  The 16 lanes of a page then transpose both 16 x 16 bit matrices at
+  // once (transpose16_step), after which lane t holds the word of coordinate
+  // pair 16 w + t of group w: coordinate 2 i in the low half, 2 i + 1 in the
+  // high half, token bits in lane order.  The top bit is NOT sign(z) and bit p
+  // below it sign(d_p) XOR sign(z), formed on the words.
+  const bool vbit_ok = valid && !vzero;
+  uint32_t vw[BV][NG];
 #pragma unroll
-  for (int p = 0; p < BV; ++p)
+  for (int gg = 0; gg < NG; ++gg) {
+    uint32_t ev[BV], od[BV];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) vm[p][q][0] = vm[p][q][1] = 0u;
-  static_for<0, D>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    const float z = x[c];
-    float dm[4];
-    magnitude_signs<BV>(fabsf(z), tv, dm);
-    const uint64_t neg = __ballot(int32_t(__float_as_uint(z)) < 0);
+    for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const float z = x[32 * gg + 2 * k + par];
+        float dm[4];
+        magnitude_signs<BV>(fabsf(z), tv, dm);
+        uint32_t(&acc)[BV] = par ? od : ev;
+        acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(z));
+#pragma unroll
+        for (int q = 0; q + 1 < BV; ++q) acc[q] = shift_in_sign(acc[q], __float_as_uint(dm[q]));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
+#pragma unroll
+    for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
+    vw[BV - 1][gg] = ~vw[BV - 1][gg];
 #pragma unroll
     for (int p = 0; p < BV; ++p) {
-      const uint64_t m = p == BV - 1 ? ~neg : __ballot(int32_t(__float_as_uint(dm[p])) < 0) ^ neg;
-      vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
-      vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
+      uint32_t w = vbit_ok ? vw[p][gg] : 0u;
+      w = transpose16_step<8>(w, lane);
+      w = transpose16_step<4>(w, lane);
+      w = transpose16_step<2>(w, lane);
+      vw[p][gg] = transpose16_step<1>(w, lane);
     }
-  });
-#pragma unroll
-  for (int p = 0; p < BV; ++p)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      vm[p][q][0] &= uint32_t(okm);
-      vm[p][q][1] &= uint32_t(okm >> 32);
-    }
+  }
   if (page_ok) *reinterpret_cast<float*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block +
                                          size_t(BV) * plane_bytes + 4 * t) = vzero ? 0.f : vnu;
-  // lane i < d/2 stores the words of coordinate pair i in each of the four pages
-  if (lane < D / 2) {
+  // lane t of page g stores the words of coordinate pairs 16 w + t of that page
+  const int pg0 = (P0 / P + g) * P;
+  const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+  if (my_phys >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
+    const uint32_t keep = keep16 | (keep16 << 16);
+    uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (phys[j] < 0) continue;
-      const int pg0 = (P0 / P + j) * P;
-      if (pg0 >= new_len) continue;
-      const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
-      if (keep16 == 0xffffu) continue;  // page holds no new token
-      const uint32_t keep = keep16 | (keep16 << 16);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[j]) * H + h) * cv.value_block) + lane * BV;
+    for (int gg = 0; gg < NG; ++gg) {
+      uint32_t* dst = base + (16 * gg + t) * BV;
       uint32_t wv[BV];
 #pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        wv[p] = __builtin_amdgcn_perm(vm[p][1][j >> 1], vm[p][0][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
-        if (keep) wv[p] = (dst[p] & keep) | wv[p];
-      }
+      for (int p = 0; p < BV; ++p) wv[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
       if constexpr (BV == 4) {
         *reinterpret_cast<uint4*>(dst) = uint4{wv[0], wv[1], wv[2], wv[3]};
       } else if constexpr (BV == 2) {
