@@ -1006,14 +1006,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 // sums per coordinate (D / 64 per lane) with several loads in flight, the
 // inverse FWHT in registers.  Dense variant: one row per workgroup, one
 // coordinate per thread, the inverse rotation as a matrix-vector product
-// through LDS.
+// through LDS.  With few rows (WIDE, FWHT only) one row takes a whole
+// workgroup instead: each wavefront sums a quarter of the splits, the partial
+// sums meet in LDS and the first wavefront finishes the row, so that a short
+// list of rows still spreads its record loads over many CUs.
 template <int ROT>
 __host__ __device__ constexpr int combine_rows(int) { return ROT == TQ_ROT_DENSE ? 1 : 4; }
-template <int D, int ROT>
+constexpr int kWideCombineRows = 512;
+template <int N>
+struct Count {
+  static constexpr int value = N;
+};  // FWHT rows up to this many: a workgroup per row
+template <int D, int ROT, bool WIDE>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
+  static_assert(!WIDE || ROT == TQ_ROT_FWHT, "the wide combine is the FWHT variant's");
   constexpr int R = D / 64;
-  constexpr int RPB = combine_rows<ROT>(0);
-  __shared__ float buf[ROT == TQ_ROT_DENSE ? D : 1];
+  constexpr int RPB = WIDE ? 1 : combine_rows<ROT>(0);
+  __shared__ float buf[ROT == TQ_ROT_DENSE ? D : (WIDE ? 4 * D : 1)];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t row = size_t(blockIdx.x) * RPB + (RPB > 1 ? wv : 0);  // s * H_q + h
   if (RPB > 1 && row >= size_t(a.num_seqs) * a.num_q_heads) return;  // whole wavefronts; no barrier on this path
@@ -1030,17 +1039,34 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
   const int nc = cv.window > 0 ? max(0, L - cv.window) : L;
   const int ns = min(a.splits, (nc + a.split_tokens - 1) / a.split_tokens);
   auto rec_of = [&](int sp) { return ws + size_t(sp < ns ? sp : a.splits) * rec; };  // the window's record last
-  // maximum and denominator over the records (every wavefront of the row alike)
-  float M = -INFINITY;
-  for (int sp = lane; sp <= ns; sp += 64) M = fmaxf(M, rec_of(sp)[0]);
-  M = wave_max(M);
-  float l = 0.f;
-  for (int sp = lane; sp <= ns; sp += 64) {
-    const float m = rec_of(sp)[0];
-    if (m != -INFINITY) l = fmaf(__expf(m - M), rec_of(sp)[1], l);
+  // maximum and denominator over the records (every wavefront of the row
+  // alike).  In the wide form with fewer than 64 compressed records, lane sp
+  // keeps record sp's weight (lane ns the window's), and the weights are
+  // broadcast from the lanes instead of being read again.
+  const bool in_lanes = WIDE && ns < 64;
+  float M = -INFINITY, l = 0.f, wl = 0.f;
+  if (in_lanes) {
+    float m = -INFINITY, lr = 0.f;
+    if (lane <= ns) {
+      const float* r = rec_of(lane);
+      m = r[0];
+      lr = r[1];
+    }
+    M = wave_max(m);
+    wl = m == -INFINITY ? 0.f : __expf(m - M);
+    l = wave_sum(wl * lr);
+  } else {
+    for (int sp = lane; sp <= ns; sp += 64) M = fmaxf(M, rec_of(sp)[0]);
+    M = wave_max(M);
+    for (int sp = lane; sp <= ns; sp += 64) {
+      const float m = rec_of(sp)[0];
+      if (m != -INFINITY) l = fmaf(__expf(m - M), rec_of(sp)[1], l);
+    }
+    l = wave_sum(l);
   }
-  l = wave_sum(l);
+  // weight of compressed split sp < ns, or of the window's record (sp = splits)
   auto weight = [&](int sp) {
+    if (in_lanes) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sp < ns ? sp : ns));
     const float m = ws[size_t(sp) * rec];
     return m == -INFINITY ? 0.f : __expf(m - M);
   };
@@ -1050,25 +1076,48 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
     float ar[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) ar[r] = 0.f;
-    constexpr int B = 32 / R;  // splits per batch: 32 loads in flight per lane
-    int sp = 0;
-    for (; sp + B <= ns; sp += B) {
-      float f[B], v[B][R];
+    constexpr int B = (WIDE ? 64 : 32) / R;  // splits per batch: loads in flight per lane
+    const int sp_beg = WIDE ? (wv * ns) / 4 : 0, sp_end = WIDE ? ((wv + 1) * ns) / 4 : ns;
+    // NB splits from sp0 with every load issued at once; past the end the
+    // last split again, with weight 0
+    auto batch = [&](auto nb, int sp0) {
+      constexpr int NB = decltype(nb)::value;
+      float f[NB], v[NB][R];
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        f[u] = weight(sp + u);
+      for (int u = 0; u < NB; ++u) {
+        const int sp = min(sp0 + u, sp_end - 1);
+        f[u] = sp0 + u < sp_end ? weight(sp) : 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) v[u][r] = ws[size_t(sp + u) * rec + 2 + r * 64 + lane];
+        for (int r = 0; r < R; ++r) v[u][r] = ws[size_t(sp) * rec + 2 + r * 64 + lane];
       }
 #pragma unroll
-      for (int u = 0; u < B; ++u)
+      for (int u = 0; u < NB; ++u)
 #pragma unroll
         for (int r = 0; r < R; ++r) ar[r] = fmaf(f[u], v[u][r], ar[r]);
+    };
+    int sp0 = sp_beg;
+    for (; sp0 + B <= sp_end; sp0 += B) batch(Count<B>{}, sp0);
+    const int rem = sp_end - sp0;
+    if constexpr (WIDE) {  // the rest in one batch of the next power of two
+      if (rem > B / 2) batch(Count<B>{}, sp0);
+      else if (rem > B / 4) batch(Count<B / 2>{}, sp0);
+      else if (rem > B / 8) batch(Count<B / 4>{}, sp0);
+      else if (rem > 2) batch(Count<4>{}, sp0);
+      else if (rem == 2) batch(Count<2>{}, sp0);
+      else if (rem == 1) batch(Count<1>{}, sp0);
+    } else {  // many rows in flight: the rest one split at a time
+      for (int sp = sp0; sp < sp_end; ++sp) batch(Count<1>{}, sp);
     }
-    for (; sp < ns; ++sp) {
-      const float f = weight(sp);
+    if constexpr (WIDE) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) ar[r] = fmaf(f, ws[size_t(sp) * rec + 2 + r * 64 + lane], ar[r]);
+      for (int r = 0; r < R; ++r) buf[wv * D + r * 64 + lane] = ar[r];
+      __syncthreads();
+      if (wv != 0) return;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int c = r * 64 + lane;
+        ar[r] = (buf[c] + buf[D + c]) + (buf[2 * D + c] + buf[3 * D + c]);
+      }
     }
     wave_fwht<R>(ar, lane);
 #pragma unroll
@@ -1126,7 +1175,13 @@ hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
-  hipLaunchKernelGGL((decode_combine_kernel<D, ROT>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a,
+  if constexpr (ROT == TQ_ROT_FWHT) {
+    if (rows <= kWideCombineRows) {
+      hipLaunchKernelGGL((decode_combine_kernel<D, ROT, true>), dim3(rows), dim3(256), 0, st, a, part_offset);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_combine_kernel<D, ROT, false>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a,
                      part_offset);
   return hipGetLastError();
 }
