@@ -25,8 +25,6 @@
 //    wavefront ballot.  Value bit-planes are stored per coordinate (16 token
 //    bits), which each lane accumulates in registers over the page's tokens and
 //    writes once.
-#include <type_traits>
-
 #include "tq_device.h"
 
 namespace tqi {
@@ -292,23 +290,6 @@ __device__ __forceinline__ void fwht_regs(float (&x)[N]) {
         x[j] = u + v;
         x[j + h] = u - v;
       }
-}
-
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// v with lane L replaced by the uniform value s (v_writelane_b32, immediate
-// lane select)
-template <int L>
-__device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t s) {
-  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(L));
-  return v;
 }
 
 // One exchange step of a 16 x 16 bit transpose over the 16 lanes of a row,
@@ -1022,58 +1003,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float tv[NVT];
 #pragma unroll
   for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * kOutScale;
-  // plane masks of this wavefront's coordinate pairs, at the lane of the pair
-  uint32_t vm[BV][2][2];
+  // value bits packed per lane and transposed across each page's 16 lanes, as
+  // in the token-per-lane kernel: after the transpose, lane ts of page pj
+  // holds the word of coordinate pair q Q / 2 + 16 gg + ts of that page
+  uint32_t vw[BV][NGQ];
 #pragma unroll
-  for (int p = 0; p < BV; ++p)
+  for (int gg = 0; gg < NGQ; ++gg) {
+    read_group(gg);
+    uint32_t ev[BV], od[BV];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) vm[p][r][0] = vm[p][r][1] = 0u;
-  // bits as wavefront masks, as in the token-per-lane kernel
-  const uint64_t okm = __ballot(vbit_ok);
-  static_for<0, Q>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    if constexpr (c % 32 == 0) read_group(c / 32);
-    const float zz = z[c % 32];
-    float dm[4];
-    magnitude_signs<BV>(fabsf(zz), tv, dm);
-    const uint64_t neg = __ballot(int32_t(__float_as_uint(zz)) < 0);
+    for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const float zz = z[2 * k + par];
+        float dm[4];
+        magnitude_signs<BV>(fabsf(zz), tv, dm);
+        uint32_t(&acc)[BV] = par ? od : ev;
+        acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(zz));
+#pragma unroll
+        for (int r = 0; r + 1 < BV; ++r) acc[r] = shift_in_sign(acc[r], __float_as_uint(dm[r]));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
+#pragma unroll
+    for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
+    vw[BV - 1][gg] = ~vw[BV - 1][gg];
 #pragma unroll
     for (int p = 0; p < BV; ++p) {
-      const uint64_t m = p == BV - 1 ? ~neg : __ballot(int32_t(__float_as_uint(dm[p])) < 0) ^ neg;
-      vm[p][c & 1][0] = set_lane<(c >> 1)>(vm[p][c & 1][0], uint32_t(m));
-      vm[p][c & 1][1] = set_lane<(c >> 1)>(vm[p][c & 1][1], uint32_t(m >> 32));
+      uint32_t w = vbit_ok ? vw[p][gg] : 0u;
+      w = transpose16_step<8>(w, lane);
+      w = transpose16_step<4>(w, lane);
+      w = transpose16_step<2>(w, lane);
+      vw[p][gg] = transpose16_step<1>(w, lane);
     }
-  });
-#pragma unroll
-  for (int p = 0; p < BV; ++p)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      vm[p][r][0] &= uint32_t(okm);
-      vm[p][r][1] &= uint32_t(okm >> 32);
-    }
+  }
   if (page_ok && q == 0)
     *reinterpret_cast<float*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block + size_t(BV) * plane_bytes +
                               4 * ts) = vbit_ok ? vnu : 0.f;
-  // lane i < Q / 2 stores the words of coordinate pair q Q / 2 + i in each page
-  if (lane < Q / 2) {
+  const int pg0 = (P0 / P + pj) * P;
+  const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+  if (phys[pj] >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
+    const uint32_t keep = keep16 | (keep16 << 16);
+    uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (phys[j] < 0) continue;
-      const int pg0 = (P0 / P + j) * P;
-      if (pg0 >= new_len) continue;
-      const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
-      if (keep16 == 0xffffu) continue;  // page holds no new token
-      const uint32_t keep = keep16 | (keep16 << 16);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[j]) * H + h) * cv.value_block) +
-                      (q * Q / 2 + lane) * BV;
-      uint32_t wv[BV];
+    for (int gg = 0; gg < NGQ; ++gg) {
+      uint32_t* dst = base + (q * Q / 2 + 16 * gg + ts) * BV;
 #pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        wv[p] = __builtin_amdgcn_perm(vm[p][1][j >> 1], vm[p][0][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
-        if (keep) wv[p] = (dst[p] & keep) | wv[p];
-      }
-#pragma unroll
-      for (int p = 0; p < BV; ++p) dst[p] = wv[p];
+      for (int p = 0; p < BV; ++p) dst[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
     }
   }
 }
