@@ -71,6 +71,17 @@ __device__ __forceinline__ void rotate(float (&x)[D / 64], const uint8_t* params
   }
 }
 
+// FWHT rotation with the role's sign bits already in registers (as masks on
+// the float sign bit): x <- scale * H D x.
+template <int R>
+__device__ __forceinline__ void fwht_rotate(float (&x)[R], const uint32_t (&sm)[R], int lane, float scale) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = __uint_as_float(__float_as_uint(x[r]) ^ sm[r]);
+  wave_fwht<R>(x, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] *= scale;
+}
+
 // QJL projection w = S e: FWHT variant S = H D2 H_n D1, dense variant S = G.
 template <int D, int ROT>
 __device__ __forceinline__ void sketch(float (&e)[D / 64], const uint8_t* params, float* lds, int lane) {
@@ -129,6 +140,19 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
   const float* piv = pik + size_t(2) * D * D;
   const float rot_scale = (ROT == TQ_ROT_FWHT) ? rsqrtf(float(D)) : 1.0f;
+  // FWHT variant: the four roles' sign bits, requested with the other
+  // parameters rather than after the page stores (which the compiler cannot
+  // move them past)
+  uint32_t sgn_k[R], sgn_s1[R], sgn_s2[R], sgn_v[R];
+  if constexpr (ROT == TQ_ROT_FWHT) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sgn_k[r] = sign_bit(a.params, kRoleKeyRot, r * 64 + lane) << 31;
+      sgn_s1[r] = sign_bit(a.params, kRoleSketch1, r * 64 + lane) << 31;
+      sgn_s2[r] = sign_bit(a.params, kRoleSketch2, r * 64 + lane) << 31;
+      sgn_v[r] = sign_bit(a.params, kRoleValueRot, r * 64 + lane) << 31;
+    }
+  }
 
   const size_t plane_bytes = size_t(P) * D / 8;
   for (int pg = start / P + part; pg * P < new_len; pg += a.parts) {
@@ -143,18 +167,34 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     for (int p = 0; p < 4; ++p)
 #pragma unroll
       for (int r = 0; r < R; ++r) vmask[p][r] = 0;
+    // value words of a page that already holds tokens: requested now, merged
+    // after the last token (no other wavefront writes this page in this call)
+    const uint32_t keep16 = (1u << (lo - pg * P)) - 1u;
+    uint32_t old[4][R];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        old[p][r] = 0u;
+        if (page_ok && keep16 != 0u && p < bv && !(lane & 1))
+          old[p][r] = reinterpret_cast<const uint32_t*>(vb)[((r * 64 + lane) / 2) * bv + p];
+      }
 
     for (int pos = lo; pos < hi; ++pos) {
       const size_t tok = size_t(b0) + (pos - start);
       const int t = pos - pg * P;
       const size_t base = (tok * H + h) * D;
       const bool in_window = W > 0 && pos >= new_len - W;
-      // ---------------- key
-      float x[R], xin[R];
+      // ---------------- key (the value row is requested with it)
+      float x[R], xin[R], vin[R];
       float ss = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         xin[r] = load_elem(a.k_new, a.dtype, base + r * 64 + lane);
+        vin[r] = load_elem(a.v_new, a.dtype, base + r * 64 + lane);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
         x[r] = xin[r];
         ss = fmaf(x[r], x[r], ss);
       }
@@ -162,7 +202,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const float nu = sqrtf(ss);
       const bool zero = !(nu >= kZeroNorm);
       const float inv = zero ? 0.f : 1.0f / nu;
-      rotate<D, ROT>(x, a.params, kRoleKeyRot, pik, lds, lane, rot_scale * inv);
+      if constexpr (ROT == TQ_ROT_FWHT) fwht_rotate<R>(x, sgn_k, lane, rot_scale * inv);
+      else rotate<D, ROT>(x, a.params, kRoleKeyRot, pik, lds, lane, rot_scale * inv);
       int idx[R];
       float e[R];
       float es = 0.f;
@@ -177,7 +218,12 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       }
       es = wave_sum(es);
       const float gamma = sqrtf(es);
-      sketch<D, ROT>(e, a.params, lds, lane);
+      if constexpr (ROT == TQ_ROT_FWHT) {
+        fwht_rotate<R>(e, sgn_s1, lane, rsqrtf(float(D)));
+        fwht_rotate<R>(e, sgn_s2, lane, 1.0f);
+      } else {
+        sketch<D, ROT>(e, a.params, lds, lane);
+      }
       if (page_ok) {
         // token row: for each 32-coordinate group, the words of all planes
         uint32_t words[4];
@@ -212,7 +258,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       ss = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        xin[r] = load_elem(a.v_new, a.dtype, base + r * 64 + lane);
+        xin[r] = vin[r];
         x[r] = xin[r];
         ss = fmaf(x[r], x[r], ss);
       }
@@ -220,7 +266,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const float vnu = sqrtf(ss);
       const bool vzero = !(vnu >= kZeroNorm);
       const float vinv = vzero ? 0.f : 1.0f / vnu;
-      rotate<D, ROT>(x, a.params, kRoleValueRot, piv, lds, lane, rot_scale * vinv);
+      if constexpr (ROT == TQ_ROT_FWHT) fwht_rotate<R>(x, sgn_v, lane, rot_scale * vinv);
+      else rotate<D, ROT>(x, a.params, kRoleValueRot, piv, lds, lane, rot_scale * vinv);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int vi = vzero ? 0 : quantize(x[r], vtr, nvt);
@@ -240,19 +287,18 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     if (page_ok) {
       // token bits below `lo` were written by earlier calls; keep them.  Value
       // words pair coordinates 2i (low half) and 2i + 1 (high half).
-      const uint32_t keep16 = (1u << (lo - pg * P)) - 1u;
       const uint32_t keep = keep16 | (keep16 << 16);
       uint32_t* words = reinterpret_cast<uint32_t*>(vb);
-      for (int p = 0; p < bv; ++p) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (p >= bv) break;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const uint32_t mine = vmask[p][r];
           const uint32_t other = __shfl_xor(mine, 1);
           if (!(lane & 1)) {
             const int c = r * 64 + lane;
-            uint32_t* w = words + (c / 2) * bv + p;
-            const uint32_t old = keep ? *w : 0u;
-            *w = (old & keep) | mine | (other << 16);
+            words[(c / 2) * bv + p] = (old[p][r] & keep) | mine | (other << 16);
           }
         }
       }
