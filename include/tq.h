@@ -23,7 +23,10 @@
  *     enqueued; tq_last_error() then describes the problem.  A launch failure
  *     reported by the HIP runtime returns TQ_ERR_HIP.  Kernels skip (never
  *     write through) page ids outside [0, num_pages), sequence slots outside
- *     [0, max_seqs) and positions beyond max_pages_per_seq * page_tokens.
+ *     [0, max_seqs) and positions beyond max_pages_per_seq * page_tokens; when
+ *     tq_cache.status is set they also report each such skip there (device-side
+ *     capacity checks, [Design Study] "Paging, lifecycle, and cache identity":
+ *     partial pages must not silently corrupt the cache).
  *   - Keys and values are [tokens, num_kv_heads, head_dim] row-major; queries
  *     are [num_seqs, num_q_heads, head_dim]; query head h reads KV head
  *     h / (num_q_heads / num_kv_heads).
@@ -97,7 +100,19 @@ typedef struct {
   int32_t max_seqs;
   int32_t max_pages_per_seq;
   int32_t reserved;
+  uint32_t* status;             /* optional device word (NULL = no reporting); kernels OR in
+                                   TQ_STATUS_* bits for work they skipped.  The caller clears
+                                   and reads it; the library never resets it. */
 } tq_cache;
+
+/* Bits of tq_cache.status. */
+enum {
+  TQ_STATUS_BAD_SLOT = 1u,   /* a sequence slot outside [0, max_seqs): that sequence was skipped */
+  TQ_STATUS_BAD_PAGE = 2u,   /* a block-table entry outside [0, num_pages) where a position was to be
+                                written or read: those tokens were skipped */
+  TQ_STATUS_CAPACITY = 4u    /* a position at or beyond max_pages_per_seq * page_tokens (append: not
+                                written), or a decode length above that or above max_ctx (clamped) */
+};
 
 /* Bytes of the parameter blob (codebooks, thresholds, signs or dense
  * matrices) that tq_init_codebooks writes.  0 for an invalid config. */
@@ -143,8 +158,13 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
                              const int32_t* cu_new_tokens, int32_t num_seqs, int32_t total_new,
                              int32_t max_new_per_seq, void* stream);
 
+/* Longest context a decode call accepts (max_ctx); larger values are
+ * rejected with TQ_ERR_CAPACITY (and a zero workspace size). */
+#define TQ_MAX_CONTEXT (1 << 30)
+
 /* Workspace bytes tq_decode_attention needs for num_seqs sequences whose
- * lengths are at most max_ctx. */
+ * lengths are at most max_ctx (0 for an invalid config or max_ctx outside
+ * [0, TQ_MAX_CONTEXT]). */
 size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t max_ctx);
 
 /* Decode attention over the compressed cache, one query per sequence
@@ -186,6 +206,10 @@ const char* tq_status_string(tq_status status);
 
 /* Human-readable detail of the last error returned on the calling thread. */
 const char* tq_last_error(void);
+
+/* Hash of the sources (include/ and the library's csrc/) this binary was
+ * built from, so that a loaded library can be matched to its source tree. */
+const char* tq_build_id(void);
 
 #ifdef __cplusplus
 }

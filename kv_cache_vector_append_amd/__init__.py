@@ -6,8 +6,13 @@ The work happens in the HIP library ``libtq_hip.so`` behind the C ABI of
 from ._lib import (  # noqa: F401
     CacheBuffers,
     Config,
+    TQ_MAX_CONTEXT,
+    TQ_STATUS_BAD_PAGE,
+    TQ_STATUS_BAD_SLOT,
+    TQ_STATUS_CAPACITY,
     TQError,
     allocate_cache,
+    build_id,
     decode_attention,
     decode_workspace_bytes,
     dequantize,

@@ -32,7 +32,8 @@ class _Config(ctypes.Structure):
 class _Cache(ctypes.Structure):
     _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("k_window", ctypes.c_void_p), ("v_window", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
-                ("max_seqs", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_seqs", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("status", ctypes.c_void_p)]
 
 
 class TQError(RuntimeError):
@@ -63,6 +64,7 @@ def load_library() -> ctypes.CDLL:
         "tq_dequantize": (I32, [cfgp, P, cachep, I32, I32, I32, P, P, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
+        "tq_build_id": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -75,7 +77,7 @@ def load_library() -> ctypes.CDLL:
 def exported_symbols():
     return ["tq_params_bytes", "tq_key_block_bytes", "tq_value_block_bytes", "tq_init_codebooks",
             "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_dequantize",
-            "tq_status_string", "tq_last_error"]
+            "tq_status_string", "tq_last_error", "tq_build_id"]
 
 
 def _check(status: int, what: str):
@@ -115,6 +117,14 @@ class Config:
                        self.page_tokens, self.window, _ROT[self.rotation], self.seed)
 
 
+TQ_STATUS_BAD_SLOT, TQ_STATUS_BAD_PAGE, TQ_STATUS_CAPACITY = 1, 2, 4
+TQ_MAX_CONTEXT = 1 << 30
+
+
+def build_id() -> str:
+    return load_library().tq_build_id().decode()
+
+
 def params_bytes(cfg: Config) -> int:
     return load_library().tq_params_bytes(ctypes.byref(cfg.c()))
 
@@ -139,11 +149,12 @@ class CacheBuffers:
     block_table: torch.Tensor   # int32 [max_seqs, max_pages_per_seq]
     k_window: torch.Tensor | None
     v_window: torch.Tensor | None
+    status: torch.Tensor | None = None   # optional int32 [1]: TQ_STATUS_* bits of skipped work
 
     def c(self) -> _Cache:
         return _Cache(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.block_table),
                       _ptr(self.k_window), _ptr(self.v_window), self.k_pages.shape[0],
-                      self.block_table.shape[0], self.block_table.shape[1], 0)
+                      self.block_table.shape[0], self.block_table.shape[1], 0, _ptr(self.status))
 
 
 def allocate_cache(cfg: Config, num_pages: int, block_table: torch.Tensor, device="cuda") -> CacheBuffers:

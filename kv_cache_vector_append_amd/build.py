@@ -9,6 +9,7 @@ library exporting the C ABI declared in include/tq.h.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import os
 import shutil
 import subprocess
@@ -39,6 +40,20 @@ COMMON = [
 FILE_FLAGS = {"tq_decode_mfma.hip": ["-fno-honor-nans"]}
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) over the library's sources: every file of
+    csrc/ and include/, in name order, with its name."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(name.encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -49,7 +64,8 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + FILE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [f'-DTQ_SOURCE_HASH="{source_hash()}"'] if src == "tq_abi.cpp" else []
+    cmd = [hipcc()] + COMMON + FILE_FLAGS.get(src, []) + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -9,6 +9,10 @@
 
 #include "tq_internal.h"
 
+#ifndef TQ_SOURCE_HASH
+#error "TQ_SOURCE_HASH (hash of the library sources) must be defined by the build"
+#endif
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -57,8 +61,12 @@ tq_status check_cache(const tq_config* c, const tq_cache* k) {
     return fail(TQ_ERR_INVALID_ARGUMENT, "cache pointers misaligned");
   if (k->num_pages <= 0 || k->max_seqs <= 0 || k->max_pages_per_seq <= 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "cache sizes must be positive");
+  if ((long long)k->max_pages_per_seq * c->page_tokens > TQ_MAX_CONTEXT)
+    return fail(TQ_ERR_CAPACITY, "max_pages_per_seq %d x %d tokens above %d", k->max_pages_per_seq, c->page_tokens,
+                TQ_MAX_CONTEXT);
   if (c->window > 0 && (!k->k_window || !k->v_window || !aligned16(k->k_window) || !aligned16(k->v_window)))
     return fail(TQ_ERR_INVALID_ARGUMENT, "window > 0 needs 16-byte aligned k_window / v_window");
+  if (k->status && !aligned4(k->status)) return fail(TQ_ERR_INVALID_ARGUMENT, "status word misaligned");
   return TQ_OK;
 }
 
@@ -77,6 +85,7 @@ tqi::CacheView view(const tq_config* c, const tq_cache* k) {
   v.window = c->window;
   v.key_block = int32_t(tqi::key_block_bytes(c->head_dim, c->key_bits, c->page_tokens));
   v.value_block = int32_t(tqi::value_block_bytes(c->head_dim, c->value_bits, c->page_tokens));
+  v.status = k->status;
   return v;
 }
 
@@ -154,7 +163,7 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
 }
 
 size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t max_ctx) {
-  if (check_config(cfg) != TQ_OK || num_seqs <= 0 || max_ctx < 0) return 0;
+  if (check_config(cfg) != TQ_OK || num_seqs <= 0 || max_ctx < 0 || max_ctx > TQ_MAX_CONTEXT) return 0;
   const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, max_ctx > 0 ? max_ctx : 1);
   const size_t partials =
       size_t(num_seqs) * cfg->num_q_heads * (p.splits + 1) * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
@@ -171,6 +180,7 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
   if (!params_dev || !aligned16(params_dev)) return fail(TQ_ERR_INVALID_ARGUMENT, "params_dev NULL or misaligned");
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARGUMENT, "bad dtype");
   if (num_seqs < 0 || max_ctx < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "negative sizes");
+  if (max_ctx > TQ_MAX_CONTEXT) return fail(TQ_ERR_CAPACITY, "max_ctx %d above %d", max_ctx, TQ_MAX_CONTEXT);
   if (num_seqs == 0) return TQ_OK;
   if (!q || !seq_slots || !ctx_len || !out || !workspace) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned4(seq_slots) || !aligned4(ctx_len))
@@ -245,5 +255,7 @@ const char* tq_status_string(tq_status s) {
 }
 
 const char* tq_last_error(void) { return g_last_error; }
+
+const char* tq_build_id(void) { return TQ_SOURCE_HASH; }
 
 }  // extern "C"

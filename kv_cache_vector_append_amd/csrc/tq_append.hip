@@ -117,7 +117,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int s = unit / H;
   if (s >= a.num_seqs) return;
   const int slot = a.seq_slots[s];
-  if (slot < 0 || slot >= cv.max_seqs) return;
+  if (slot < 0 || slot >= cv.max_seqs) {
+    report(cv.status, true, TQ_STATUS_BAD_SLOT);
+    return;
+  }
   const int start = a.ctx_len_before[s];
   const int b0 = a.cu_new_tokens[s];
   const int n = a.cu_new_tokens[s + 1] - b0;
@@ -156,9 +159,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 
   const size_t plane_bytes = size_t(P) * D / 8;
   for (int pg = start / P + part; pg * P < new_len; pg += a.parts) {
-    if (pg >= cv.max_pages_per_seq) break;
+    if (pg >= cv.max_pages_per_seq) {
+      report(cv.status, true, TQ_STATUS_CAPACITY);
+      break;
+    }
     const int phys = cv.block_table[size_t(slot) * cv.max_pages_per_seq + pg];
     const bool page_ok = phys >= 0 && phys < cv.num_pages;
+    report(cv.status, !page_ok, TQ_STATUS_BAD_PAGE);
     const int lo = max(start, pg * P), hi = min(new_len, (pg + 1) * P);
     uint8_t* kb = cv.k_pages + (size_t(phys) * H + h) * cv.key_block;
     uint8_t* vb = cv.v_pages + (size_t(phys) * H + h) * cv.value_block;
@@ -490,228 +497,235 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   const int s = unit / H;
   if (s >= a.num_seqs) return;
   const int slot = a.seq_slots[s];
-  if (slot < 0 || slot >= cv.max_seqs) return;
+  if (slot < 0 || slot >= cv.max_seqs) {
+    report(cv.status, true, TQ_STATUS_BAD_SLOT);
+    return;
+  }
   const int start = a.ctx_len_before[s];
   const int b0 = a.cu_new_tokens[s];
   const int n = a.cu_new_tokens[s + 1] - b0;
   if (n <= 0 || start < 0) return;
   const int new_len = start + n;
-  const int P0 = (start / 64 + chunk) * 64;
-  if (P0 >= new_len) return;
-  const int pos = P0 + lane;
-  const bool valid = pos >= start && pos < new_len;
-  const int g = lane >> 4, t = lane & 15;
+  // chunks chunk, chunk + parts, ...: every 64-position chunk of the new
+  // tokens is written whatever max_new_per_seq the launch was sized with
+  for (int P0 = (start / 64 + chunk) * 64; P0 < new_len; P0 += a.parts * 64) {
+    const int pos = P0 + lane;
+    const bool valid = pos >= start && pos < new_len;
+    const int g = lane >> 4, t = lane & 15;
 
-  // the four pages of this chunk (uniform ids through the scalar cache)
-  const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
-  int phys[4];
+    // the four pages of this chunk (uniform ids through the scalar cache)
+    const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
+    int phys[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pg = P0 / P + j;
-    const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
-    phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
-  }
-  int my_phys = phys[0];
-  my_phys = g == 1 ? phys[1] : my_phys;
-  my_phys = g == 2 ? phys[2] : my_phys;
-  my_phys = g == 3 ? phys[3] : my_phys;
-  const bool page_ok = valid && my_phys >= 0;
-  const bool in_window = valid && W > 0 && pos >= new_len - W;
-  const size_t row = (size_t(b0) + (pos - start)) * H + h;
-
-  const const_f32* prm = (const const_f32*)a.params;
-  // the four sign vectors (roles KR, KS1, KS2, VR), read through the scalar cache
-  const const_u32* sgn_words = (const const_u32*)(a.params + kOffSigns);
-  auto sgn = [&](int role) { return sgn_words + role * (kSignRoleBytes / 4); };
-  const float sqd = sqrtf(float(D));
-  const size_t plane_bytes = size_t(P) * D / 8;
-
-  float x[D];
-  // ------------------------------------------------------------------ key
-  if (valid) {
-    load_row<D>(a.k_new, a.dtype, row, x);
-  } else {
-#pragma unroll
-    for (int c = 0; c < D; ++c) x[c] = 0.f;
-  }
-  if (in_window) store_f16_row<D>(cv.k_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
-  const float nu = sqrtf(ss);
-  const bool zero = !(nu >= kZeroNorm);
-  const float kscale = zero ? 0.f : sqd * nu;
-  float tk[NKT], ck[NKC];
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kscale;
-#pragma unroll
-  for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kscale;
-  phase();
-  flip_signs<D>(x, sgn(kRoleKeyRot));
-  fwht_regs<D>(x);
-  phase();
-  // codes, residual e = z - c[idx] (in place), its norm
-  uint32_t kw[MK + 1][NG];
-  float es = 0.f;
-#pragma unroll
-  for (int gg = 0; gg < NG; ++gg) {
-#pragma unroll
-    for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
-#pragma unroll
-    for (int k = 31; k >= 0; --k) {
-      const int c = 32 * gg + k;
-      const float z = x[c];
-      const uint32_t zb = __float_as_uint(z);
-      float dm[4];
-      magnitude_signs<MK>(fabsf(z), tk, dm);
-      // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
-      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
-#pragma unroll
-      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
-      const float e = z - __builtin_copysignf(centroid_mag<MK>(ck, dm), z);
-      x[c] = e;
-      es = fmaf(e, e, es);
-      // keep the words and the sum current here (the compiler would otherwise
-      // defer them and hold every z and e alive)
-#pragma unroll
-      for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
-      asm volatile("" : "+v"(es));
+    for (int j = 0; j < 4; ++j) {
+      const int pg = P0 / P + j;
+      const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
+      phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
+      if (cv.status != nullptr && lane == 0 && pg * P < new_len && (pg + 1) * P > start && phys[j] < 0)
+        report(cv.status, true, pg < cv.max_pages_per_seq ? TQ_STATUS_BAD_PAGE : TQ_STATUS_CAPACITY);
     }
-#pragma unroll
-    for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
-    kw[MK - 1][gg] = ~kw[MK - 1][gg];
-  }
-  const float gamma = sqrtf(es) * (zero ? 0.f : 1.f / kscale);
-  phase();
-  // QJL: z = [S e < 0] with S = H D2 H_n D1 (the positive factors drop out)
-  flip_signs<D>(x, sgn(kRoleSketch1));
-  fwht_regs<D>(x);
-  flip_signs<D>(x, sgn(kRoleSketch2));
-  fwht_regs<D>(x);
-  phase();
-#pragma unroll
-  for (int gg = 0; gg < NG; ++gg) {
-    uint32_t q = 0u;
-#pragma unroll
-    for (int k = 31; k >= 0; --k) {
-      q = shift_in_sign(q, __float_as_uint(x[32 * gg + k]));
-      asm volatile("" : "+v"(q));
-    }
-    kw[MK][gg] = zero ? 0u : q;
-  }
-  if (zero) {
-#pragma unroll
-    for (int p = 0; p < MK; ++p)
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) kw[p][gg] = 0u;
-  }
-  uint8_t* kb = page_ok ? cv.k_pages + (size_t(my_phys) * H + h) * cv.key_block : nullptr;
-  if (page_ok) {
-    // token row: for each 32-coordinate group, the words of all planes
-    uint32_t wr[KWORDS];
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg)
-#pragma unroll
-      for (int p = 0; p <= MK; ++p) wr[gg * (MK + 1) + p] = kw[p][gg];
-    uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * KWORDS * 4);
-    if constexpr (KWORDS % 4 == 0) {
-#pragma unroll
-      for (int q = 0; q < KWORDS / 4; ++q)
-        reinterpret_cast<uint4*>(dst)[q] = uint4{wr[4 * q], wr[4 * q + 1], wr[4 * q + 2], wr[4 * q + 3]};
+    int my_phys = phys[0];
+    my_phys = g == 1 ? phys[1] : my_phys;
+    my_phys = g == 2 ? phys[2] : my_phys;
+    my_phys = g == 3 ? phys[3] : my_phys;
+    const bool page_ok = valid && my_phys >= 0;
+    const bool in_window = valid && W > 0 && pos >= new_len - W;
+    const size_t row = (size_t(b0) + (pos - start)) * H + h;
+
+    const const_f32* prm = (const const_f32*)a.params;
+    // the four sign vectors (roles KR, KS1, KS2, VR), read through the scalar cache
+    const const_u32* sgn_words = (const const_u32*)(a.params + kOffSigns);
+    auto sgn = [&](int role) { return sgn_words + role * (kSignRoleBytes / 4); };
+    const float sqd = sqrtf(float(D));
+    const size_t plane_bytes = size_t(P) * D / 8;
+
+    float x[D];
+    // ------------------------------------------------------------------ key
+    if (valid) {
+      load_row<D>(a.k_new, a.dtype, row, x);
     } else {
 #pragma unroll
-      for (int q = 0; q < KWORDS / 2; ++q) reinterpret_cast<uint2*>(dst)[q] = uint2{wr[2 * q], wr[2 * q + 1]};
+      for (int c = 0; c < D; ++c) x[c] = 0.f;
     }
-    *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * t) =
-        make_float2(zero ? 0.f : nu, gamma);
-  }
-
-  // ------------------------------------------------------------------ value
-  phase();
-  if (valid) {
-    load_row<D>(a.v_new, a.dtype, row, x);
-  } else {
+    if (in_window) store_f16_row<D>(cv.k_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
+    float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) x[c] = 0.f;
-  }
-  if (in_window) store_f16_row<D>(cv.v_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
-  ss = 0.f;
+    for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
+    const float nu = sqrtf(ss);
+    const bool zero = !(nu >= kZeroNorm);
+    const float kscale = zero ? 0.f : sqd * nu;
+    float tk[NKT], ck[NKC];
 #pragma unroll
-  for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
-  const float vnu = sqrtf(ss);
-  const bool vzero = !(vnu >= kZeroNorm);
-  const float vscale = vzero ? 0.f : sqd * vnu;
-  float tv[NVT];
+    for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kscale;
 #pragma unroll
-  for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * vscale;
-  phase();
-  flip_signs<D>(x, sgn(kRoleValueRot));
-  fwht_regs<D>(x);
-  phase();
-  // Value bits in the page layout (per coordinate pair, the 16 token bits of
-  // each coordinate) without ballots.  Each lane packs its own token's bits
-  // of a 32-coordinate group into one word per plane, even coordinates in the
-  // low half and odd ones in the high half: bit k of a half is coordinate pair
-  // k.  The 16 lanes of a page then transpose both 16 x 16 bit matrices at
-  // once (transpose16_step), after which lane t holds the word of coordinate
-  // pair 16 w + t of group w: coordinate 2 i in the low half, 2 i + 1 in the
-  // high half, token bits in lane order.  The top bit is NOT sign(z) and bit p
-  // below it sign(d_p) XOR sign(z), formed on the words.
-  const bool vbit_ok = valid && !vzero;
-  uint32_t vw[BV][NG];
-#pragma unroll
-  for (int gg = 0; gg < NG; ++gg) {
-    uint32_t ev[BV], od[BV];
-#pragma unroll
-    for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
-#pragma unroll
-    for (int k = 15; k >= 0; --k) {
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const float z = x[32 * gg + 2 * k + par];
-        float dm[4];
-        magnitude_signs<BV>(fabsf(z), tv, dm);
-        uint32_t(&acc)[BV] = par ? od : ev;
-        acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(z));
-#pragma unroll
-        for (int q = 0; q + 1 < BV; ++q) acc[q] = shift_in_sign(acc[q], __float_as_uint(dm[q]));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
-#pragma unroll
-    for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
-    vw[BV - 1][gg] = ~vw[BV - 1][gg];
-#pragma unroll
-    for (int p = 0; p < BV; ++p) {
-      uint32_t w = vbit_ok ? vw[p][gg] : 0u;
-      w = transpose16_step<8>(w, lane);
-      w = transpose16_step<4>(w, lane);
-      w = transpose16_step<2>(w, lane);
-      vw[p][gg] = transpose16_step<1>(w, lane);
-    }
-  }
-  if (page_ok) *reinterpret_cast<float*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block +
-                                         size_t(BV) * plane_bytes + 4 * t) = vzero ? 0.f : vnu;
-  // lane t of page g stores the words of coordinate pairs 16 w + t of that page
-  const int pg0 = (P0 / P + g) * P;
-  const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
-  if (my_phys >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
-    const uint32_t keep = keep16 | (keep16 << 16);
-    uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block);
+    for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kscale;
+    phase();
+    flip_signs<D>(x, sgn(kRoleKeyRot));
+    fwht_regs<D>(x);
+    phase();
+    // codes, residual e = z - c[idx] (in place), its norm
+    uint32_t kw[MK + 1][NG];
+    float es = 0.f;
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-      uint32_t* dst = base + (16 * gg + t) * BV;
-      uint32_t wv[BV];
 #pragma unroll
-      for (int p = 0; p < BV; ++p) wv[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
-      if constexpr (BV == 4) {
-        *reinterpret_cast<uint4*>(dst) = uint4{wv[0], wv[1], wv[2], wv[3]};
-      } else if constexpr (BV == 2) {
-        *reinterpret_cast<uint2*>(dst) = uint2{wv[0], wv[1]};
+      for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
+#pragma unroll
+      for (int k = 31; k >= 0; --k) {
+        const int c = 32 * gg + k;
+        const float z = x[c];
+        const uint32_t zb = __float_as_uint(z);
+        float dm[4];
+        magnitude_signs<MK>(fabsf(z), tk, dm);
+        // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
+        kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
+#pragma unroll
+        for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
+        const float e = z - __builtin_copysignf(centroid_mag<MK>(ck, dm), z);
+        x[c] = e;
+        es = fmaf(e, e, es);
+        // keep the words and the sum current here (the compiler would otherwise
+        // defer them and hold every z and e alive)
+#pragma unroll
+        for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
+        asm volatile("" : "+v"(es));
+      }
+#pragma unroll
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
+      kw[MK - 1][gg] = ~kw[MK - 1][gg];
+    }
+    const float gamma = sqrtf(es) * (zero ? 0.f : 1.f / kscale);
+    phase();
+    // QJL: z = [S e < 0] with S = H D2 H_n D1 (the positive factors drop out)
+    flip_signs<D>(x, sgn(kRoleSketch1));
+    fwht_regs<D>(x);
+    flip_signs<D>(x, sgn(kRoleSketch2));
+    fwht_regs<D>(x);
+    phase();
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      uint32_t q = 0u;
+#pragma unroll
+      for (int k = 31; k >= 0; --k) {
+        q = shift_in_sign(q, __float_as_uint(x[32 * gg + k]));
+        asm volatile("" : "+v"(q));
+      }
+      kw[MK][gg] = zero ? 0u : q;
+    }
+    if (zero) {
+#pragma unroll
+      for (int p = 0; p < MK; ++p)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) kw[p][gg] = 0u;
+    }
+    uint8_t* kb = page_ok ? cv.k_pages + (size_t(my_phys) * H + h) * cv.key_block : nullptr;
+    if (page_ok) {
+      // token row: for each 32-coordinate group, the words of all planes
+      uint32_t wr[KWORDS];
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+        for (int p = 0; p <= MK; ++p) wr[gg * (MK + 1) + p] = kw[p][gg];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * KWORDS * 4);
+      if constexpr (KWORDS % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < KWORDS / 4; ++q)
+          reinterpret_cast<uint4*>(dst)[q] = uint4{wr[4 * q], wr[4 * q + 1], wr[4 * q + 2], wr[4 * q + 3]};
       } else {
 #pragma unroll
-        for (int p = 0; p < BV; ++p) dst[p] = wv[p];
+        for (int q = 0; q < KWORDS / 2; ++q) reinterpret_cast<uint2*>(dst)[q] = uint2{wr[2 * q], wr[2 * q + 1]};
+      }
+      *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * t) =
+          make_float2(zero ? 0.f : nu, gamma);
+    }
+
+    // ------------------------------------------------------------------ value
+    phase();
+    if (valid) {
+      load_row<D>(a.v_new, a.dtype, row, x);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D; ++c) x[c] = 0.f;
+    }
+    if (in_window) store_f16_row<D>(cv.v_window + ((size_t(slot) * H + h) * W + (pos % W)) * D, x);
+    ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) ss = fmaf(x[c], x[c], ss);
+    const float vnu = sqrtf(ss);
+    const bool vzero = !(vnu >= kZeroNorm);
+    const float vscale = vzero ? 0.f : sqd * vnu;
+    float tv[NVT];
+#pragma unroll
+    for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * vscale;
+    phase();
+    flip_signs<D>(x, sgn(kRoleValueRot));
+    fwht_regs<D>(x);
+    phase();
+    // Value bits in the page layout (per coordinate pair, the 16 token bits of
+    // each coordinate) without ballots.  Each lane packs its own token's bits
+    // of a 32-coordinate group into one word per plane, even coordinates in the
+    // low half and odd ones in the high half: bit k of a half is coordinate pair
+    // k.  The 16 lanes of a page then transpose both 16 x 16 bit matrices at
+    // once (transpose16_step), after which lane t holds the word of coordinate
+    // pair 16 w + t of group w: coordinate 2 i in the low half, 2 i + 1 in the
+    // high half, token bits in lane order.  The top bit is NOT sign(z) and bit p
+    // below it sign(d_p) XOR sign(z), formed on the words.
+    const bool vbit_ok = valid && !vzero;
+    uint32_t vw[BV][NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      uint32_t ev[BV], od[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
+#pragma unroll
+      for (int k = 15; k >= 0; --k) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          const float z = x[32 * gg + 2 * k + par];
+          float dm[4];
+          magnitude_signs<BV>(fabsf(z), tv, dm);
+          uint32_t(&acc)[BV] = par ? od : ev;
+          acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(z));
+#pragma unroll
+          for (int q = 0; q + 1 < BV; ++q) acc[q] = shift_in_sign(acc[q], __float_as_uint(dm[q]));
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
+#pragma unroll
+      for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
+      vw[BV - 1][gg] = ~vw[BV - 1][gg];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        uint32_t w = vbit_ok ? vw[p][gg] : 0u;
+        w = transpose16_step<8>(w, lane);
+        w = transpose16_step<4>(w, lane);
+        w = transpose16_step<2>(w, lane);
+        vw[p][gg] = transpose16_step<1>(w, lane);
+      }
+    }
+    if (page_ok) *reinterpret_cast<float*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block +
+                                           size_t(BV) * plane_bytes + 4 * t) = vzero ? 0.f : vnu;
+    // lane t of page g stores the words of coordinate pairs 16 w + t of that page
+    const int pg0 = (P0 / P + g) * P;
+    const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+    if (my_phys >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
+      const uint32_t keep = keep16 | (keep16 << 16);
+      uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(my_phys) * H + h) * cv.value_block);
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        uint32_t* dst = base + (16 * gg + t) * BV;
+        uint32_t wv[BV];
+#pragma unroll
+        for (int p = 0; p < BV; ++p) wv[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
+        if constexpr (BV == 4) {
+          *reinterpret_cast<uint4*>(dst) = uint4{wv[0], wv[1], wv[2], wv[3]};
+        } else if constexpr (BV == 2) {
+          *reinterpret_cast<uint2*>(dst) = uint2{wv[0], wv[1]};
+        } else {
+#pragma unroll
+          for (int p = 0; p < BV; ++p) dst[p] = wv[p];
+        }
       }
     }
   }
@@ -857,249 +871,256 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int s = unit / H;
   if (s >= a.num_seqs) return;
   const int slot = a.seq_slots[s];
-  if (slot < 0 || slot >= cv.max_seqs) return;
+  if (slot < 0 || slot >= cv.max_seqs) {
+    report(cv.status, true, TQ_STATUS_BAD_SLOT);
+    return;
+  }
   const int start = a.ctx_len_before[s];
   const int b0 = a.cu_new_tokens[s];
   const int n = a.cu_new_tokens[s + 1] - b0;
   if (n <= 0 || start < 0) return;
   const int new_len = start + n;
-  const int P0 = (start / T + chunk) * T;
-  if (P0 >= new_len) return;  // uniform: no barrier has been reached
-
-  const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
-  int phys[4];
+  // chunks chunk, chunk + parts, ... (uniform per workgroup): every chunk of
+  // the new tokens is written whatever max_new_per_seq the launch was sized with
+  for (int P0 = (start / T + chunk) * T; P0 < new_len; P0 += a.parts * T) {
+    const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
+    int phys[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pg = P0 / P + j;
-    const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
-    phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
-  }
-  const const_f32* prm = (const const_f32*)a.params;
-  const _Float16* m16 = reinterpret_cast<const _Float16*>(a.params + dense16_offset(D, 0));
-  const size_t mm = size_t(D) * D;  // halves per fp16 matrix
-  const size_t plane_bytes = size_t(P) * D / 8;
-
-  // token rows [P0, P0 + 64) of src into the LDS block as fp16 pieces of
-  // 2^10 x / nu; norms to nrm (0 outside [start, new_len)); fp16 ring copies of
-  // window rows.  Wavefront q stages tokens 16 q .. 16 q + 15, LPT lanes per row.
-  auto stage = [&](const void* src, uint16_t* ring) {
-    constexpr int NP = 16 / TPP;  // passes
-    // every pass's 8 elements first (one uniform dtype branch), so that the
-    // loads are in flight together
-    uint32_t raw[NP][8];
-#pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-      const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
-      const int pos = P0 + t;
-      const size_t e0 = ((size_t(b0) + (pos - start)) * H + h) * D + 8 * sub;
-      const bool valid = pos >= start && pos < new_len;
-      if (a.dtype == TQ_F32) {
-        const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const float*>(src) + e0);
-        const uint4 u = valid ? p4[0] : uint4{0u, 0u, 0u, 0u}, v = valid ? p4[1] : uint4{0u, 0u, 0u, 0u};
-        raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
-        raw[pass][4] = v.x; raw[pass][5] = v.y; raw[pass][6] = v.z; raw[pass][7] = v.w;
-      } else {
-        const uint4 u = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e0)
-                              : uint4{0u, 0u, 0u, 0u};
-        raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int pg = P0 / P + j;
+      const int ph = pg < cv.max_pages_per_seq ? bt[pg] : -1;
+      phys[j] = (ph >= 0 && ph < cv.num_pages) ? ph : -1;
+      if (cv.status != nullptr && lane == 0 && pg * P < new_len && (pg + 1) * P > start && phys[j] < 0)
+        report(cv.status, true, pg < cv.max_pages_per_seq ? TQ_STATUS_BAD_PAGE : TQ_STATUS_CAPACITY);
     }
+    const const_f32* prm = (const const_f32*)a.params;
+    const _Float16* m16 = reinterpret_cast<const _Float16*>(a.params + dense16_offset(D, 0));
+    const size_t mm = size_t(D) * D;  // halves per fp16 matrix
+    const size_t plane_bytes = size_t(P) * D / 8;
+
+    // token rows [P0, P0 + 64) of src into the LDS block as fp16 pieces of
+    // 2^10 x / nu; norms to nrm (0 outside [start, new_len)); fp16 ring copies of
+    // window rows.  Wavefront q stages tokens 16 q .. 16 q + 15, LPT lanes per row.
+    auto stage = [&](const void* src, uint16_t* ring) {
+      constexpr int NP = 16 / TPP;  // passes
+      // every pass's 8 elements first (one uniform dtype branch), so that the
+      // loads are in flight together
+      uint32_t raw[NP][8];
 #pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-      const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
-      const int pos = P0 + t;
-      const bool valid = pos >= start && pos < new_len;
-      float x[8];
-      if (a.dtype == TQ_F32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(raw[pass][e]);
-      } else if (a.dtype == TQ_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = __uint_as_float(raw[pass][i] << 16);
-          x[2 * i + 1] = __uint_as_float(raw[pass][i] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = f16_bits_to_float(uint16_t(raw[pass][i] & 0xffffu));
-          x[2 * i + 1] = f16_bits_to_float(uint16_t(raw[pass][i] >> 16));
+      for (int pass = 0; pass < NP; ++pass) {
+        const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
+        const int pos = P0 + t;
+        const size_t e0 = ((size_t(b0) + (pos - start)) * H + h) * D + 8 * sub;
+        const bool valid = pos >= start && pos < new_len;
+        if (a.dtype == TQ_F32) {
+          const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const float*>(src) + e0);
+          const uint4 u = valid ? p4[0] : uint4{0u, 0u, 0u, 0u}, v = valid ? p4[1] : uint4{0u, 0u, 0u, 0u};
+          raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
+          raw[pass][4] = v.x; raw[pass][5] = v.y; raw[pass][6] = v.z; raw[pass][7] = v.w;
+        } else {
+          const uint4 u = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e0)
+                                : uint4{0u, 0u, 0u, 0u};
+          raw[pass][0] = u.x; raw[pass][1] = u.y; raw[pass][2] = u.z; raw[pass][3] = u.w;
         }
       }
-      if (valid && W > 0 && pos >= new_len - W) {
-        uint32_t w4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w4[i] = uint32_t(float_to_f16_bits(x[2 * i])) | (uint32_t(float_to_f16_bits(x[2 * i + 1])) << 16);
-        *reinterpret_cast<uint4*>(ring + ((size_t(slot) * H + h) * W + (pos % W)) * D + 8 * sub) =
-            uint4{w4[0], w4[1], w4[2], w4[3]};
+      for (int pass = 0; pass < NP; ++pass) {
+        const int t = 16 * q + pass * TPP + lane / LPT, sub = lane % LPT;
+        const int pos = P0 + t;
+        const bool valid = pos >= start && pos < new_len;
+        float x[8];
+        if (a.dtype == TQ_F32) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(raw[pass][e]);
+        } else if (a.dtype == TQ_BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(raw[pass][i] << 16);
+            x[2 * i + 1] = __uint_as_float(raw[pass][i] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[2 * i] = f16_bits_to_float(uint16_t(raw[pass][i] & 0xffffu));
+            x[2 * i + 1] = f16_bits_to_float(uint16_t(raw[pass][i] >> 16));
+          }
+        }
+        if (valid && W > 0 && pos >= new_len - W) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w4[i] = uint32_t(float_to_f16_bits(x[2 * i])) | (uint32_t(float_to_f16_bits(x[2 * i + 1])) << 16);
+          *reinterpret_cast<uint4*>(ring + ((size_t(slot) * H + h) * W + (pos % W)) * D + 8 * sub) =
+              uint4{w4[0], w4[1], w4[2], w4[3]};
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+        for (int o = 1; o < LPT; o <<= 1) ss += __shfl_xor(ss, o);
+        const float nu = sqrtf(ss);
+        const float sc = nu >= kZeroNorm ? kRowScale / nu : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= sc;
+        store_pieces(buf + t * DT::ROWB + 32 * sub, x);
+        if (sub == 0) nrm[t] = valid && nu >= kZeroNorm ? nu : 0.f;
       }
-      float ss = 0.f;
+    };
+    auto gemm_to_rows = [&](int m) {
+      f4v acc[DT::CT][4];
+      block_barrier();  // rows staged
+      dense_gemm<D>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc);
+      block_barrier();  // every wavefront has read the rows
+      dense_store<D>(acc, buf, q, lane);
+      block_barrier();  // products visible
+    };
+    // this lane's token, 32 coordinates of this wavefront's quarter
+    float z[32];
+    auto read_group = [&](int gg) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-      for (int o = 1; o < LPT; o <<= 1) ss += __shfl_xor(ss, o);
-      const float nu = sqrtf(ss);
-      const float sc = nu >= kZeroNorm ? kRowScale / nu : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= sc;
-      store_pieces(buf + t * DT::ROWB + 32 * sub, x);
-      if (sub == 0) nrm[t] = valid && nu >= kZeroNorm ? nu : 0.f;
-    }
-  };
-  auto gemm_to_rows = [&](int m) {
-    f4v acc[DT::CT][4];
-    block_barrier();  // rows staged
-    dense_gemm<D>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc);
-    block_barrier();  // every wavefront has read the rows
-    dense_store<D>(acc, buf, q, lane);
-    block_barrier();  // products visible
-  };
-  // this lane's token, 32 coordinates of this wavefront's quarter
-  float z[32];
-  auto read_group = [&](int gg) {
-#pragma unroll
-    for (int c = 0; c < 32; c += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(buf + lane * DT::ROWB + (q * Q + 32 * gg + c) * 4);
-      z[c] = v.x; z[c + 1] = v.y; z[c + 2] = v.z; z[c + 3] = v.w;
-    }
-  };
-
-  const int t = lane, pos = P0 + t;
-  const bool valid = pos >= start && pos < new_len;
-  const int pj = t >> 4, ts = t & 15;
-  const bool page_ok = valid && phys[pj] >= 0;
-
-  // ------------------------------------------------------------------ key
-  stage(a.k_new, cv.k_window);
-  gemm_to_rows(0);
-  const float nu = nrm[t];
-  const bool zero = !(nu > 0.f);
-  float tk[NKT], ck[NKC];
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kOutScale;
-#pragma unroll
-  for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kOutScale;
-  uint32_t kw[MK + 1][NGQ];
-  float es = 0.f;
-#pragma unroll
-  for (int gg = 0; gg < NGQ; ++gg) {
-    read_group(gg);
-#pragma unroll
-    for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
-#pragma unroll
-    for (int k = 31; k >= 0; --k) {
-      const int c = k;
-      const float zz = z[c];
-      const uint32_t zb = __float_as_uint(zz);
-      float dm[4];
-      magnitude_signs<MK>(fabsf(zz), tk, dm);
-      // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
-      kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
-#pragma unroll
-      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
-      const float e = zz - __builtin_copysignf(centroid_mag<MK>(ck, dm), zz);
-      z[c] = e;
-      es = fmaf(e, e, es);
-      // keep the words and the sum current (deferred, every decision would stay live)
-#pragma unroll
-      for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
-      asm volatile("" : "+v"(es));
-      if ((k & 7) == 0) {  // the 8 residuals of this block (as 2^12 e), over their fp32 source
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = z[c + i] * kResidualScale;
-        store_pieces(buf + t * DT::ROWB + (q * Q + 32 * gg + c) * 4, v);
+      for (int c = 0; c < 32; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(buf + lane * DT::ROWB + (q * Q + 32 * gg + c) * 4);
+        z[c] = v.x; z[c + 1] = v.y; z[c + 2] = v.z; z[c + 3] = v.w;
       }
-    }
-#pragma unroll
-    for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
-    kw[MK - 1][gg] = ~kw[MK - 1][gg];
-  }
-  esum[q][t] = es;
-  // QJL: signs of w = G e
-  gemm_to_rows(1);
-#pragma unroll
-  for (int gg = 0; gg < NGQ; ++gg) {
-    read_group(gg);
-    uint32_t qb = 0u;
-#pragma unroll
-    for (int k = 31; k >= 0; --k) qb = shift_in_sign(qb, __float_as_uint(z[k]));
-    kw[MK][gg] = qb;
-  }
-  if (page_ok) {
-    uint8_t* kb = cv.k_pages + (size_t(phys[pj]) * H + h) * cv.key_block;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(ts) * KWORDS * 4) + q * NGQ * (MK + 1);
-#pragma unroll
-    for (int gg = 0; gg < NGQ; ++gg)
-#pragma unroll
-      for (int p = 0; p <= MK; ++p) dst[gg * (MK + 1) + p] = zero ? 0u : kw[p][gg];
-    if (q == 0) {
-      const float gamma = zero ? 0.f : sqrtf(esum[0][t] + esum[1][t] + esum[2][t] + esum[3][t]) * (1.f / kOutScale);
-      *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * ts) = make_float2(zero ? 0.f : nu, gamma);
-    }
-  }
-  block_barrier();  // key products consumed, norms read
+    };
 
-  // ------------------------------------------------------------------ value
-  stage(a.v_new, cv.v_window);
-  gemm_to_rows(2);
-  const float vnu = nrm[t];
-  const bool vbit_ok = valid && vnu > 0.f;
-  float tv[NVT];
+    const int t = lane, pos = P0 + t;
+    const bool valid = pos >= start && pos < new_len;
+    const int pj = t >> 4, ts = t & 15;
+    const bool page_ok = valid && phys[pj] >= 0;
+
+    // ------------------------------------------------------------------ key
+    stage(a.k_new, cv.k_window);
+    gemm_to_rows(0);
+    const float nu = nrm[t];
+    const bool zero = !(nu > 0.f);
+    float tk[NKT], ck[NKC];
 #pragma unroll
-  for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * kOutScale;
-  // value bits packed per lane and transposed across each page's 16 lanes, as
-  // in the token-per-lane kernel: after the transpose, lane ts of page pj
-  // holds the word of coordinate pair q Q / 2 + 16 gg + ts of that page
-  uint32_t vw[BV][NGQ];
+    for (int j = 0; j < NKT; ++j) tk[j] = prm[kOffKeyThresholds / 4 + (1 << (MK - 1)) + j] * kOutScale;
 #pragma unroll
-  for (int gg = 0; gg < NGQ; ++gg) {
-    read_group(gg);
-    uint32_t ev[BV], od[BV];
-#pragma unroll
-    for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
-#pragma unroll
-    for (int k = 15; k >= 0; --k) {
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const float zz = z[2 * k + par];
-        float dm[4];
-        magnitude_signs<BV>(fabsf(zz), tv, dm);
-        uint32_t(&acc)[BV] = par ? od : ev;
-        acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(zz));
-#pragma unroll
-        for (int r = 0; r + 1 < BV; ++r) acc[r] = shift_in_sign(acc[r], __float_as_uint(dm[r]));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
-#pragma unroll
-    for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
-    vw[BV - 1][gg] = ~vw[BV - 1][gg];
-#pragma unroll
-    for (int p = 0; p < BV; ++p) {
-      uint32_t w = vbit_ok ? vw[p][gg] : 0u;
-      w = transpose16_step<8>(w, lane);
-      w = transpose16_step<4>(w, lane);
-      w = transpose16_step<2>(w, lane);
-      vw[p][gg] = transpose16_step<1>(w, lane);
-    }
-  }
-  if (page_ok && q == 0)
-    *reinterpret_cast<float*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block + size_t(BV) * plane_bytes +
-                              4 * ts) = vbit_ok ? vnu : 0.f;
-  const int pg0 = (P0 / P + pj) * P;
-  const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
-  if (phys[pj] >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
-    const uint32_t keep = keep16 | (keep16 << 16);
-    uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block);
+    for (int j = 0; j < NKC; ++j) ck[j] = prm[kOffKeyCentroids / 4 + (1 << (MK - 1)) + j] * kOutScale;
+    uint32_t kw[MK + 1][NGQ];
+    float es = 0.f;
 #pragma unroll
     for (int gg = 0; gg < NGQ; ++gg) {
-      uint32_t* dst = base + (q * Q / 2 + 16 * gg + ts) * BV;
+      read_group(gg);
 #pragma unroll
-      for (int p = 0; p < BV; ++p) dst[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
+      for (int p = 0; p <= MK; ++p) kw[p][gg] = 0u;
+#pragma unroll
+      for (int k = 31; k >= 0; --k) {
+        const int c = k;
+        const float zz = z[c];
+        const uint32_t zb = __float_as_uint(zz);
+        float dm[4];
+        magnitude_signs<MK>(fabsf(zz), tk, dm);
+        // sign(z) and sign(d_p) alone; the XOR and the inversion follow per word
+        kw[MK - 1][gg] = shift_in_sign(kw[MK - 1][gg], zb);
+#pragma unroll
+        for (int p = 0; p + 1 < MK; ++p) kw[p][gg] = shift_in_sign(kw[p][gg], __float_as_uint(dm[p]));
+        const float e = zz - __builtin_copysignf(centroid_mag<MK>(ck, dm), zz);
+        z[c] = e;
+        es = fmaf(e, e, es);
+        // keep the words and the sum current (deferred, every decision would stay live)
+#pragma unroll
+        for (int p = 0; p < MK; ++p) asm volatile("" : "+v"(kw[p][gg]));
+        asm volatile("" : "+v"(es));
+        if ((k & 7) == 0) {  // the 8 residuals of this block (as 2^12 e), over their fp32 source
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = z[c + i] * kResidualScale;
+          store_pieces(buf + t * DT::ROWB + (q * Q + 32 * gg + c) * 4, v);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p + 1 < MK; ++p) kw[p][gg] ^= kw[MK - 1][gg];
+      kw[MK - 1][gg] = ~kw[MK - 1][gg];
     }
+    esum[q][t] = es;
+    // QJL: signs of w = G e
+    gemm_to_rows(1);
+#pragma unroll
+    for (int gg = 0; gg < NGQ; ++gg) {
+      read_group(gg);
+      uint32_t qb = 0u;
+#pragma unroll
+      for (int k = 31; k >= 0; --k) qb = shift_in_sign(qb, __float_as_uint(z[k]));
+      kw[MK][gg] = qb;
+    }
+    if (page_ok) {
+      uint8_t* kb = cv.k_pages + (size_t(phys[pj]) * H + h) * cv.key_block;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(ts) * KWORDS * 4) + q * NGQ * (MK + 1);
+#pragma unroll
+      for (int gg = 0; gg < NGQ; ++gg)
+#pragma unroll
+        for (int p = 0; p <= MK; ++p) dst[gg * (MK + 1) + p] = zero ? 0u : kw[p][gg];
+      if (q == 0) {
+        const float gamma = zero ? 0.f : sqrtf(esum[0][t] + esum[1][t] + esum[2][t] + esum[3][t]) * (1.f / kOutScale);
+        *reinterpret_cast<float2*>(kb + size_t(MK + 1) * plane_bytes + 8 * ts) = make_float2(zero ? 0.f : nu, gamma);
+      }
+    }
+    block_barrier();  // key products consumed, norms read
+
+    // ------------------------------------------------------------------ value
+    stage(a.v_new, cv.v_window);
+    gemm_to_rows(2);
+    const float vnu = nrm[t];
+    const bool vbit_ok = valid && vnu > 0.f;
+    float tv[NVT];
+#pragma unroll
+    for (int j = 0; j < NVT; ++j) tv[j] = prm[kOffValueThresholds / 4 + (1 << (BV - 1)) + j] * kOutScale;
+    // value bits packed per lane and transposed across each page's 16 lanes, as
+    // in the token-per-lane kernel: after the transpose, lane ts of page pj
+    // holds the word of coordinate pair q Q / 2 + 16 gg + ts of that page
+    uint32_t vw[BV][NGQ];
+#pragma unroll
+    for (int gg = 0; gg < NGQ; ++gg) {
+      read_group(gg);
+      uint32_t ev[BV], od[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) ev[p] = od[p] = 0u;
+#pragma unroll
+      for (int k = 15; k >= 0; --k) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          const float zz = z[2 * k + par];
+          float dm[4];
+          magnitude_signs<BV>(fabsf(zz), tv, dm);
+          uint32_t(&acc)[BV] = par ? od : ev;
+          acc[BV - 1] = shift_in_sign(acc[BV - 1], __float_as_uint(zz));
+#pragma unroll
+          for (int r = 0; r + 1 < BV; ++r) acc[r] = shift_in_sign(acc[r], __float_as_uint(dm[r]));
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < BV; ++p) vw[p][gg] = (od[p] << 16) | ev[p];
+#pragma unroll
+      for (int p = 0; p + 1 < BV; ++p) vw[p][gg] ^= vw[BV - 1][gg];
+      vw[BV - 1][gg] = ~vw[BV - 1][gg];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        uint32_t w = vbit_ok ? vw[p][gg] : 0u;
+        w = transpose16_step<8>(w, lane);
+        w = transpose16_step<4>(w, lane);
+        w = transpose16_step<2>(w, lane);
+        vw[p][gg] = transpose16_step<1>(w, lane);
+      }
+    }
+    if (page_ok && q == 0)
+      *reinterpret_cast<float*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block + size_t(BV) * plane_bytes +
+                                4 * ts) = vbit_ok ? vnu : 0.f;
+    const int pg0 = (P0 / P + pj) * P;
+    const uint32_t keep16 = start > pg0 ? (start - pg0 >= P ? 0xffffu : (1u << (start - pg0)) - 1u) : 0u;
+    if (phys[pj] >= 0 && pg0 < new_len && keep16 != 0xffffu) {  // the page holds a new token
+      const uint32_t keep = keep16 | (keep16 << 16);
+      uint32_t* base = reinterpret_cast<uint32_t*>(cv.v_pages + (size_t(phys[pj]) * H + h) * cv.value_block);
+#pragma unroll
+      for (int gg = 0; gg < NGQ; ++gg) {
+        uint32_t* dst = base + (q * Q / 2 + 16 * gg + ts) * BV;
+#pragma unroll
+        for (int p = 0; p < BV; ++p) dst[p] = keep ? (dst[p] & keep) | vw[p][gg] : vw[p][gg];
+      }
+    }
+    block_barrier();  // LDS rows and norms are rewritten by the next chunk
   }
 }
 

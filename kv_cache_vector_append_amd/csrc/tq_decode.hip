@@ -77,6 +77,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   const int slot = a.seq_slots[s];
   int L = a.ctx_len[s];
+  if (cv.status != nullptr && split == 0 && tid == 0) {
+    report(cv.status, slot < 0 || slot >= cv.max_seqs, TQ_STATUS_BAD_SLOT);
+    report(cv.status, L < 0 || L > min(cv.max_pages_per_seq * P, a.max_ctx), TQ_STATUS_CAPACITY);
+  }
   if (slot < 0 || slot >= cv.max_seqs || L < 0) L = 0;
   if (L > cv.max_pages_per_seq * P) L = cv.max_pages_per_seq * P;
   if (L > a.max_ctx) L = a.max_ctx;
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       if (valid) {
         const int phys = cv.block_table[size_t(slot) * cv.max_pages_per_seq + pos / P];
         page_ok = phys >= 0 && phys < cv.num_pages;
+        report(cv.status, !page_ok, TQ_STATUS_BAD_PAGE);
         if (page_ok) {
           const uint8_t* kb = cv.k_pages + (size_t(phys) * H + h) * cv.key_block;
           const int t = pos % P;

@@ -542,12 +542,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // working margin (scores, addresses) calibrated on the compiled kernels.
 // Two wavefronts per SIMD leave 256.
 constexpr int kRegBudget = 256;
-#ifndef TQ_REG_MARGIN
-#define TQ_REG_MARGIN 68
-#endif
+constexpr int kRegMargin = 68;
 __host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds) {
   return num_planes(BV) * (D / 16 / NW) * 4 + (q_in_lds ? 0 : (num_planes(MK) + 1) * (D / 128) * 8) +
-         (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + TQ_REG_MARGIN;
+         (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + kRegMargin;
 }
 __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
   return (D / 16) % NW == 0 && 8 % NW == 0 && ((D / 16) / NW) % 2 == 0;
@@ -562,11 +560,8 @@ __host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, boo
 // SIMD: at d = 128 with at most two value bits one wavefront per work item
 // measured faster than four at four per SIMD, whose recent-token window then
 // runs on one of the four.
-#ifndef TQ_SPLIT_OCC3
-#define TQ_SPLIT_OCC3 1
-#endif
 __host__ __device__ constexpr int split_occupancy(int D, int MK, int BV) {
-  return TQ_SPLIT_OCC3 && D == 128 && BV > 2 ? 3 : 2;
+  return D == 128 && BV > 2 ? 3 : 2;
 }
 // Variants where the estimate above is too optimistic (the compiled loop
 // spills at the estimated count) and the wavefront count that compiles clean.
@@ -598,21 +593,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   constexpr int PPW = 8 / NW;          // pages scored per wavefront per block
   constexpr int KW = (MK + 1) * KH;    // key words per lane per page
   constexpr int VW = (CBW / 2) * BV;   // value words per lane per page pair
-#ifndef TQ_PAGE_FENCE
-#define TQ_PAGE_FENCE 0
-#endif
-  // scheduling fences between page pairs of the scores: off by default (the
-  // compiler interleaves more pages across the chained MFMAs), kept where the
-  // extra pages in flight would spill (d = 256, 3 key MSE bits, 2 value bits)
-  constexpr bool kPageFence = TQ_PAGE_FENCE || (D == 256 && MK == 3 && BV == 2);
-#ifndef TQ_PLANE_OUTER
-#define TQ_PLANE_OUTER 1
-#endif
-  constexpr bool kPlaneOuter = TQ_PLANE_OUTER && QL && PPW <= 4;  // eight pages of accumulators would spill
-#ifndef TQ_ROLL_KEYS
-#define TQ_ROLL_KEYS 1
-#endif
-  constexpr bool kRollKeys = TQ_ROLL_KEYS && !kPlaneOuter;  // key pages re-requested one by one
+  // scheduling fences between page pairs of the scores, only where the extra
+  // pages in flight would spill (d = 256, 3 key MSE bits, 2 value bits);
+  // elsewhere the compiler interleaves more pages across the chained MFMAs
+  constexpr bool kPageFence = D == 256 && MK == 3 && BV == 2;
+  constexpr bool kPlaneOuter = QL && PPW <= 4;  // eight pages of accumulators would spill
+  constexpr bool kRollKeys = !kPlaneOuter;  // key pages re-requested one by one
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
@@ -635,6 +621,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 
   const int slot = a.seq_slots[s];
   int L = a.ctx_len[s];
+  if (cv.status != nullptr && split == 0 && tid == 0) {
+    report(cv.status, slot < 0 || slot >= cv.max_seqs, TQ_STATUS_BAD_SLOT);
+    report(cv.status, L < 0 || L > min(cv.max_pages_per_seq * kPage, a.max_ctx), TQ_STATUS_CAPACITY);
+  }
   if (slot < 0 || slot >= cv.max_seqs || L < 0) L = 0;
   if (L > cv.max_pages_per_seq * kPage) L = cv.max_pages_per_seq * kPage;
   if (L > a.max_ctx) L = a.max_ctx;
@@ -841,6 +831,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       const float qsum = (dq[j][0] + dq[j][1]) + (dq[j][2] + dq[j][3]);
       const float est = knj.x * fmaf(knj.y, qsum, msum);
       const bool tok_ok = pos < t_end && kok[j];
+      if (cv.status != nullptr) report(cv.status, pos < t_end && !kok[j], TQ_STATUS_BAD_PAGE);
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? est : -INFINITY;
       vnu[j] = tok_ok ? vnj : 0.f;

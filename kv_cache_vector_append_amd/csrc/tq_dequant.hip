@@ -59,6 +59,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a) {
   const int pg = pos / P, t = pos % P;
   const int phys = (pg < cv.max_pages_per_seq) ? cv.block_table[size_t(a.seq_slot) * cv.max_pages_per_seq + pg] : -1;
   if (phys < 0 || phys >= cv.num_pages) {
+    report(cv.status, lane == 0, TQ_STATUS_BAD_PAGE);
 #pragma unroll
     for (int r = 0; r < R; ++r) ko[r * 64 + lane] = vo[r * 64 + lane] = 0.f;
     return;

@@ -26,6 +26,12 @@ __device__ __forceinline__ float load_elem(const void* base, int dtype, size_t i
   return dtype == TQ_BF16 ? bf16_bits_to_float(b) : f16_bits_to_float(b);
 }
 
+// Debug capacity check: ORs `bits` into the caller's status word (when one
+// was given) from every lane where `bad` holds.
+__device__ __forceinline__ void report(uint32_t* status, bool bad, uint32_t bits) {
+  if (status != nullptr && bad) atomicOr(status, bits);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

@@ -230,17 +230,19 @@ SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
   const int units = (num_seqs > 0 ? num_seqs : 1) * cfg.num_kv_heads;
   const int tile = mfma ? 128 : 64;
   const int items = mfma ? decode_mfma_items(cfg) : 2048;
-  const int max_tiles = (max_ctx + tile - 1) / tile;
-  int splits = (items + units - 1) / units;
+  // 64-bit arithmetic: max_ctx may be up to TQ_MAX_CONTEXT
+  const long long ctx = max_ctx > 0 ? max_ctx : 1;
+  const long long max_tiles = (ctx + tile - 1) / tile;
+  long long splits = (items + units - 1) / units;
   if (splits > max_tiles) splits = max_tiles;
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
-  const int per = (max_ctx + splits - 1) / splits;
-  int split_tokens = ((per + tile - 1) / tile) * tile;
+  const long long per = (ctx + splits - 1) / splits;
+  long long split_tokens = ((per + tile - 1) / tile) * tile;
   if (split_tokens < tile) split_tokens = tile;
-  splits = (max_ctx + split_tokens - 1) / split_tokens;
+  splits = (ctx + split_tokens - 1) / split_tokens;
   if (splits < 1) splits = 1;
-  return {splits, split_tokens};
+  return {int(splits), int(split_tokens)};
 }
 
 void build_params(const tq_config& cfg, uint8_t* blob) {

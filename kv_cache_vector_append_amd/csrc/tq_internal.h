@@ -79,6 +79,7 @@ struct CacheView {
   int32_t num_pages, max_seqs, max_pages_per_seq;
   int32_t num_kv_heads, page_tokens, window;
   int32_t key_block, value_block;  // bytes
+  uint32_t* status;                // optional TQ_STATUS_* word
 };
 
 struct AppendArgs {

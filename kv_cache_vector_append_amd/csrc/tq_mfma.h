@@ -65,12 +65,9 @@ __device__ __forceinline__ v4f mfma_f4_f8(const v8i& a, const v8i& b, v4f acc, i
 // i.e. the other operand carries the factor f_j and a per-row constant is
 // added to the product.
 __device__ __forceinline__ v8i bits_to_fp4_affine(uint32_t w) {
-#ifndef TQ_KEY_BITOP3
-#define TQ_KEY_BITOP3 1
-#endif
+  // dword 3 = (w & 0x88888888) | 0x22222222 in one bitop3
   const v4i lo = {int(w & 0x11111111u), int(w & 0x22222222u), int(w & 0x44444444u),
-                  TQ_KEY_BITOP3 ? int(__builtin_amdgcn_bitop3_b32(w, 0x88888888u, 0x22222222u, 0xEA))  // (w & 0x8..) | 0x2..
-                                : int((w & 0x88888888u) | 0x22222222u)};
+                  int(__builtin_amdgcn_bitop3_b32(w, 0x88888888u, 0x22222222u, 0xEA))};
   // an fp4 operand occupies the low four registers; the upper four are not read
   return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
 }

@@ -6,7 +6,7 @@ Parity rules:
     coordinate lies within 1e-6 of a threshold (counted, reported); for a token
     with such a flip, the QJL bits are re-derived from the GPU's codes, and a
     bit may differ only where |w_j| / sqrt(d) < 1e-6;
-  * fp32 norms agree to a relative 1e-5 (fp32 vs fp64 arithmetic);
+  * fp32 norms agree to a relative 1e-6 (fp32 vs fp64 arithmetic);
   * the fp16 window is bit-exact;
   * decode: max over (seq, head) rows of max|o_gpu - o_ref| / max|o_ref| <= 2e-3.
 """
@@ -21,7 +21,7 @@ import workloads
 from oracle import tq
 
 BAND = 1e-6
-NORM_RTOL = 1e-5
+NORM_RTOL = 1e-6
 DECODE_TOL = 2e-3
 
 
@@ -55,8 +55,11 @@ class Run:
     block_table: np.ndarray | None = None
 
 
-def make_run(w: workloads.Workload, lens, chunks=1, oracle_append=True, device="cuda", P=None):
-    """Append `lens[i]` tokens to sequence i on the GPU (in `chunks` calls) and in the oracle."""
+def make_run(w: workloads.Workload, lens, chunks=1, oracle_append=True, device="cuda", P=None, max_new=None):
+    """Append `lens[i]` tokens to sequence i on the GPU (in `chunks` calls) and in the oracle.
+
+    max_new: the max_new_per_seq each append call passes (default: the true
+    largest count; any value >= 1 is allowed and must give the same bytes)."""
     tqa = lib()
     cfg = lib_config(w)
     ocfg = oracle_config(w)
@@ -82,7 +85,7 @@ def make_run(w: workloads.Workload, lens, chunks=1, oracle_append=True, device="
         if kn.shape[0] == 0:
             continue
         i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
-        maxn = max(cu[i + 1] - cu[i] for i in range(nseq))
+        maxn = max_new or max(cu[i + 1] - cu[i] for i in range(nseq))
         tqa.quantize_append(cfg, params, cache, kn, vn, i32(list(range(nseq))), i32(before), i32(cu), maxn)
         if oracle_append:
             tq.append(P, ocache, torch.cat(ks).double().numpy(), torch.cat(vs).double().numpy(),
@@ -181,13 +184,17 @@ def compare_append(run: Run, gc: tq.Cache | None = None, positions=None) -> Appe
 
 def aligned_oracle_cache(run: Run, gc: tq.Cache | None = None):
     """The oracle's own cache, except that where the GPU took the other side of a
-    near-threshold (|y - t| < 1e-6) code decision, the oracle adopts the GPU's codes
-    and recomputes that token's residual norm and QJL bits itself in float64.
+    near-threshold decision, the oracle adopts the GPU's decision:
+      * a code with |y - t| < 1e-6: the oracle takes the GPU's codes and
+        recomputes that token's residual norm and QJL bits itself in float64;
+      * a QJL bit with |w_j| / sqrt(d) < 1e-6 (the sign decision's threshold
+        is 0): the oracle takes the GPU's bit.
 
     Returns (cache, number of token-heads adjusted).  An end-to-end decode over
     this cache is the oracle's result under the same band decisions; without it
-    one excused flip on a token holding much of the softmax mass can move the
-    output far more than the decode tolerance.
+    a few excused flips on tokens holding much of the softmax mass move the
+    output far more than the decode tolerance (57 in-band QJL flips among the
+    60M sign bits of 64 x 1024 head_dim-256 tokens move it by 1e-2).
     """
     import copy
     gc = gc if gc is not None else gpu_cache_as_oracle(run)
@@ -214,6 +221,18 @@ def aligned_oracle_cache(run: Run, gc: tq.Cache | None = None):
             oc.k_codes[pg[i], h, t[i]] = codes
             oc.k_z[pg[i], h, t[i]] = w < 0
             oc.k_gamma[pg[i], h, t[i]] = np.float32(np.linalg.norm(e))
+            adjusted += 1
+        # QJL bits on the (now aligned) codes: adopt in-band sign decisions
+        o = oc.gather(s, pos)
+        zm = (g["k_z"] != o["k_z"]).any(axis=-1)
+        for (i, h) in np.argwhere(zm):
+            ek = tq.encode_keys(P, run.K[s][i, h].double().numpy()[None])
+            e = ek["y"][0] - P.kc[o["k_codes"][i, h].astype(np.int64)]
+            w = P.T.sketch(e[None])[0]
+            diff = g["k_z"][i, h] != o["k_z"][i, h]
+            if ek["nu"][0] == 0 or not np.all(np.abs(w[diff]) / np.sqrt(d) < BAND):
+                continue                                           # a real mismatch stays visible
+            oc.k_z[pg[i], h, t[i]] = g["k_z"][i, h]
             adjusted += 1
         vm = (g["v_codes"] != o["v_codes"]).any(axis=-1)
         for (i, h) in np.argwhere(vm):

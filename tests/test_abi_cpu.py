@@ -112,7 +112,7 @@ def test_calls_validate_before_touching_a_device():
     cfg = tqa.Config(128, 32, 8, 3, 2, 16, 128, "fwht", 1).c()
     # NULL cache, NULL params, misaligned pointers, too-small workspace: all host-side errors
     assert lib.tq_quantize_append(ctypes.byref(cfg), None, None, None, None, 1, None, None, None, 1, 1, 1, None) == 1
-    cache = tqa._lib._Cache(16, 16, 16, 16, 16, 4, 1, 4, 0)
+    cache = tqa._lib._Cache(16, 16, 16, 16, 16, 4, 1, 4, 0, None)
     assert lib.tq_quantize_append(ctypes.byref(cfg), 16, ctypes.byref(cache), 17, 16, 1, 16, 16, 16, 1, 1, 1,
                                   None) == 1
     assert lib.tq_decode_attention(ctypes.byref(cfg), 16, ctypes.byref(cache), 16, 1, 16, 16, 1, 100, 0.0, 16, 16,
@@ -124,3 +124,30 @@ def test_calls_validate_before_touching_a_device():
     # empty work is a no-op that succeeds without a device
     assert lib.tq_quantize_append(ctypes.byref(cfg), 16, ctypes.byref(cache), 16, 16, 1, 16, 16, 16, 0, 0, 1,
                                   None) == 0
+
+
+def test_build_id_matches_the_sources():
+    """The loaded library was built from the sources in this tree."""
+    from kv_cache_vector_append_amd import build
+    assert _tqa().build_id() == build.source_hash()
+
+
+def test_context_limit_is_rejected_on_the_host():
+    tqa = _tqa()
+    lib = tqa.load_library()
+    cfg = tqa.Config(128, 32, 8, 3, 2, 16, 128, "fwht", 1)
+    # the split plan is computed in 64 bits up to the limit, and refused beyond it
+    assert tqa.decode_workspace_bytes(cfg, 2, tqa.TQ_MAX_CONTEXT) > 0
+    assert tqa.decode_workspace_bytes(cfg, 2, tqa.TQ_MAX_CONTEXT + 1) == 0
+    assert tqa.decode_workspace_bytes(cfg, 2, 2 ** 31 - 1) == 0
+    c = cfg.c()
+    cache = tqa._lib._Cache(16, 16, 16, 16, 16, 4, 1, 4, 0, None)
+    assert lib.tq_decode_attention(ctypes.byref(c), 16, ctypes.byref(cache), 16, 1, 16, 16, 1, 2 ** 31 - 1, 0.0,
+                                   16, 16, 1 << 40, None, None) == 3
+    assert b"max_ctx" in lib.tq_last_error()
+    # a cache whose pages per sequence exceed the limit is refused as well
+    big = tqa._lib._Cache(16, 16, 16, 16, 16, 4, 1, (1 << 26) + 1, 0, None)
+    assert lib.tq_dequantize(ctypes.byref(c), 16, ctypes.byref(big), 0, 0, 1, 16, 16, None) == 3
+    # a misaligned status word is an argument error
+    odd = tqa._lib._Cache(16, 16, 16, 16, 16, 4, 1, 4, 0, 18)
+    assert lib.tq_dequantize(ctypes.byref(c), 16, ctypes.byref(odd), 0, 0, 1, 16, 16, None) == 1

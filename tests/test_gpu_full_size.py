@@ -14,7 +14,14 @@ it checks what it can compute piece by piece:
     bytes of every token of that head (a cache holding that head alone) and
     the GPU's output for the head's query group must agree within DECODE_TOL;
     the logits the kernel dumps are checked at sampled positions of every
-    query head against the oracle's estimate from the same bytes.
+    query head against the oracle's estimate from the same bytes;
+  * on the outlier workload, that head's output cosine, and the Spearman rank
+    correlation and Recall@8 of its logits, against the oracle (agreement) and
+    against exact attention over the raw keys and values (quality).
+
+Workloads: outlier stress (4 x 131072, d = 128, 4/4-bit, FWHT), head_dim 256
+(8 x 32768, dense rotation, 3/2- and 4/4-bit) and the mixed serving step
+(64 x 4096 appended, 256 x 4096 decoded).
 """
 import numpy as np
 import pytest
@@ -96,7 +103,8 @@ def _check_append(w, P, cache, bt, samples, inputs):
 
 def _check_decode_head(w, cache, bt, slot, hk, L, q, out_gpu):
     """Oracle decode of one kv head of one sequence over the GPU's bytes of that
-    head, against the GPU output of the head's query group."""
+    head, against the GPU output of the head's query group.  Returns the error,
+    the oracle's output rows [G, d] and its logits [G, L]."""
     G, d, W = w.gqa, w.head_dim, w.window
     cfg1 = _ocfg(w, num_q_heads=G, num_kv_heads=1)
     P1 = tq.Params(cfg1)
@@ -112,7 +120,20 @@ def _check_decode_head(w, cache, bt, slot, hk, L, q, out_gpu):
     c.load_bytes(kb, vb, kwin, vwin)
     qg = q[slot, hk * G:(hk + 1) * G].double().cpu().numpy()[None]
     ref, lg = tq.decode(P1, c, qg, [0], [L], return_logits=True)
-    return decode_error(out_gpu[slot, hk * G:(hk + 1) * G][None], ref), lg[0]
+    return decode_error(out_gpu[slot, hk * G:(hk + 1) * G][None], ref), ref[0], lg[0]
+
+
+def _rank_metrics(a, b, k=8):
+    """Per row: cosine of two outputs is computed elsewhere; here Spearman rho of
+    two logit rows and the overlap of their top-k positions (Recall@k)."""
+    from scipy.stats import spearmanr
+    rho = [spearmanr(x, y).correlation for x, y in zip(a, b)]
+    rec = [len(set(np.argsort(-x)[:k]) & set(np.argsort(-y)[:k])) / k for x, y in zip(a, b)]
+    return float(np.mean(rho)), float(np.min(rho)), float(np.mean(rec)), float(np.min(rec))
+
+
+def _cos(a, b):
+    return (a * b).sum(-1) / np.linalg.norm(a, axis=-1) / np.linalg.norm(b, axis=-1)
 
 
 def _decode(S, cache, logits=None):
@@ -152,13 +173,18 @@ def _logit_samples(w, S, cache, bt, slot, rng):
     return worst
 
 
-def test_full_size_outlier_stress_decode():
-    """4 x 131072 tokens, 32 q / 8 KV heads, 4/4-bit, FWHT: the default bench workload."""
+def _full_size_decode(name, head, logit_slot, quality=False):
+    """The decode workload `name` at full size in bench.py's launch
+    configuration: sampled append token-heads, one kv head decoded over all its
+    tokens from the GPU's bytes, sampled logits; with `quality`, also the rank
+    and output agreement of that head with the oracle and with exact attention
+    over its raw keys and values."""
     import kv_cache_vector_append_amd as tqa
-    w = workloads.WORKLOADS["outlier_stress"]
+    w = workloads.WORKLOADS[name]
     torch.cuda.set_device(DEV)
     S = bench.build_decode_setup(w, tqa, torch, DEV)
     nseq, ctx = w.decode_seqs, w.decode_ctx
+    hs, hk = head
     # the timed step: append token ctx - 1 of every sequence, decode over ctx tokens
     tqa.quantize_append(S.cfg, S.params, S.cache, S.step_k, S.step_v, *S.app_args)
     out = _decode(S, S.cache)
@@ -167,6 +193,7 @@ def test_full_size_outlier_stress_decode():
     rng = np.random.default_rng(20241)
     samples = {s: _sample_positions(w, ctx, rng) for s in range(nseq)}
     inputs = {s: ([], []) for s in range(nseq)}
+    head_k, head_v = [], []
     g = workloads.device_generator(w, 1, DEV)
     chunk = 16384
     for start in range(0, ctx - 1, chunk):
@@ -178,6 +205,9 @@ def test_full_size_outlier_stress_decode():
             rows = torch.from_numpy(s * n + sel - start).to(DEV)
             inputs[s][0].append(k[rows].double().cpu().numpy())
             inputs[s][1].append(v[rows].double().cpu().numpy())
+        if quality:
+            head_k.append(k[hs * n:(hs + 1) * n, hk].double().cpu().numpy())
+            head_v.append(v[hs * n:(hs + 1) * n, hk].double().cpu().numpy())
         del k, v
     step_k = workloads.device_kv(w, "k", nseq, g, DEV)
     step_v = workloads.device_kv(w, "v", nseq, g, DEV)
@@ -191,12 +221,45 @@ def test_full_size_outlier_stress_decode():
     bt = S.cache.block_table.cpu().numpy()
     P = tq.Params(_ocfg(w))
     flips = _check_append(w, P, S.cache, bt, samples, inputs)
-    err, _ = _check_decode_head(w, S.cache, bt, 2, 5, ctx, S.q, out)
-    worst = _logit_samples(w, S, S.cache, bt, 1, rng)
-    print(f"[full size] outlier_stress: {sum(len(p) for p in samples.values()) * w.num_kv_heads} sampled "
-          f"token-heads ({flips} band flips), decode err {err:.3g} (seq 2, kv head 5, {ctx} tokens), "
+    err, ref, lg_ref = _check_decode_head(w, S.cache, bt, hs, hk, ctx, S.q, out)
+    worst = _logit_samples(w, S, S.cache, bt, logit_slot, rng)
+    print(f"[full size] {name}: {sum(len(p) for p in samples.values()) * w.num_kv_heads} sampled "
+          f"token-heads ({flips} band flips), decode err {err:.3g} (seq {hs}, kv head {hk}, {ctx} tokens), "
           f"logit rel err {worst:.3g}", flush=True)
     assert err <= DECODE_TOL
+    if not quality:
+        return
+    G, d = w.gqa, w.head_dim
+    logits = torch.full((nseq, w.num_q_heads, S.max_ctx), float("nan"), device=DEV)
+    _decode(S, S.cache, logits)
+    lg_gpu = logits[hs, hk * G:(hk + 1) * G].double().cpu().numpy()
+    o_gpu = out[hs, hk * G:(hk + 1) * G]
+    Kh = np.concatenate(head_k + [step_k[hs:hs + 1, hk].double().cpu().numpy()])
+    Vh = np.concatenate(head_v + [step_v[hs:hs + 1, hk].double().cpu().numpy()])
+    qh = S.q[hs, hk * G:(hk + 1) * G].double().cpu().numpy()
+    lg_exact = qh @ Kh.T / np.sqrt(d)
+    o_exact = tq.exact_attention(qh, Kh, Vh, 1 / np.sqrt(d))
+    vs_oracle = (float(_cos(o_gpu, ref).min()),) + _rank_metrics(lg_gpu, lg_ref)
+    vs_exact = (float(_cos(o_gpu, o_exact).min()),) + _rank_metrics(lg_gpu, lg_exact)
+    for what, m in (("oracle", vs_oracle), ("exact attention", vs_exact)):
+        print(f"[full size] {name} vs {what}: cos_sim min {m[0]:.6f}; Spearman rho mean {m[1]:.5f} min {m[2]:.5f}; "
+              f"Recall@8 mean {m[3]:.3f} min {m[4]:.3f} (seq {hs}, kv head {hk}, {G} query heads, {ctx} tokens)",
+              flush=True)
+    # against the oracle: the same computation, so the same ranking
+    assert vs_oracle[0] > 1 - 1e-5 and vs_oracle[2] > 0.9999 and vs_oracle[4] >= 7 / 8
+    # against exact attention: quality, at the bars [README] "Paper Validation" sets
+    assert vs_exact[1] > 0.85 and vs_exact[3] >= 0.40
+
+
+def test_full_size_outlier_stress_decode():
+    """4 x 131072 tokens, 32 q / 8 KV heads, 4/4-bit, FWHT: the default bench workload."""
+    _full_size_decode("outlier_stress", head=(2, 5), logit_slot=1, quality=True)
+
+
+@pytest.mark.parametrize("name", ["hd256_long_dense_3_2", "hd256_long_dense_4_4"])
+def test_full_size_head_dim_256_dense_decode(name):
+    """8 x 32768 tokens, 16 q / 4 KV heads, head_dim 256, dense rotation (matrix-core append)."""
+    _full_size_decode(name, head=(5, 3), logit_slot=6)
 
 
 def test_full_size_mixed_serving_step():

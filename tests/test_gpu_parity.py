@@ -17,21 +17,34 @@ from harness import (DECODE_TOL, NORM_RTOL, aligned_oracle_cache, compare_append
 
 pytestmark = pytest.mark.gpu
 
+def _ragged(n, top, spread, step=37):
+    """n lengths, the first equal to `top` (the decode's max_ctx), the rest ragged below it."""
+    return [top] + [top - (s * step) % spread for s in range(1, n)]
+
+
+# case name -> (workload, lengths, append calls)
 CASES = {
-    "tiny_ref": ([1024], 1),
-    "gqa_decode": ([700, 129, 1000], 1),
-    "hd256_long_dense_3_2": ([300, 77], 1),
-    "hd256_long_dense_4_4": ([300, 77], 2),
-    "hd256_long_fwht_3_2": ([257, 31], 1),
-    "outlier_stress": ([520, 260, 1], 1),
-    "mixed_serving": ([400, 3, 160, 0], 3),
+    "tiny_ref": ("tiny_ref", [1024], 1),
+    "gqa_decode": ("gqa_decode", [700, 129, 1000], 1),
+    "hd256_long_dense_3_2": ("hd256_long_dense_3_2", [300, 77], 1),
+    "hd256_long_dense_4_4": ("hd256_long_dense_4_4", [300, 77], 2),
+    "hd256_long_fwht_3_2": ("hd256_long_fwht_3_2", [257, 31], 1),
+    # head_dim 256 with enough sequences that the decode's split plan gives
+    # every split several 128-token blocks (2, 8 and 2 per split): the online
+    # softmax re-base, the next-block prefetch and the cross-wavefront merge
+    # run across blocks
+    "hd256_dense_3_2_multiblock": ("hd256_long_dense_3_2", _ragged(64, 1024, 200), 1),
+    "hd256_dense_4_4_multiblock": ("hd256_long_dense_4_4", _ragged(16, 4096, 700), 2),
+    "hd256_fwht_3_2_multiblock": ("hd256_long_fwht_3_2", _ragged(64, 1024, 300), 1),
+    "outlier_stress": ("outlier_stress", [520, 260, 1], 1),
+    "mixed_serving": ("mixed_serving", [400, 3, 160, 0], 3),
     # shapes outside the matrix-core kernel (head_dim 64, GQA group of 8) use the plain kernels
-    "plain_hd64_gqa8": ([300, 130], 2),
-    "plain_hd128_gqa8": ([200, 50], 1),
+    "plain_hd64_gqa8": ("plain_hd64_gqa8", [300, 130], 2),
+    "plain_hd128_gqa8": ("plain_hd128_gqa8", [200, 50], 1),
     # dense rotation, appends of a few tokens per call (partial matrix-core tiles)
-    "dense_short_appends": ([40, 13], 8),
+    "dense_short_appends": ("dense_short_appends", [40, 13], 8),
     # dense rotation at head_dim 64 (the wavefront-per-token kernel)
-    "dense_hd64": ([100, 37], 3),
+    "dense_hd64": ("dense_hd64", [100, 37], 3),
 }
 
 import workloads as _w
@@ -51,8 +64,8 @@ _PARAMS = {}
 
 def _run(name):
     if name not in _RUNS:
-        w = workloads.WORKLOADS[name]
-        lens, chunks = CASES[name]
+        wname, lens, chunks = CASES[name]
+        w = workloads.WORKLOADS[wname]
         print(f"[parity] append {name} lens={lens} chunks={chunks}", flush=True)
         key = (w.head_dim, w.key_bits, w.value_bits, w.rotation)
         run = make_run(w, lens, chunks=chunks, P=_PARAMS.get(key))
@@ -148,10 +161,11 @@ def test_append_is_deterministic():
             assert np.array_equal(ga[key], gb[key]), key
 
 
-def test_edge_cases_zero_vectors_and_single_tokens():
+def test_edge_cases_single_tokens_and_page_edges():
+    # lengths 1, 16, 17 and 33 appended in two calls: single tokens, a full
+    # page, one token past a page edge, pages completed across calls
     w = workloads.TINY_REF.replace(num_q_heads=2, num_kv_heads=1, window=16, input_dtype="f32")
     run = make_run(w, [1, 16, 17, 33], chunks=2)
-    # overwrite: zero keys/values for one position via a second append of a fresh sequence slot
     rep = compare_append(run)
     assert rep.unexcused == 0 and rep.window_mismatch == 0
     q = queries(w, 4)
@@ -209,3 +223,74 @@ def test_zero_rows_inside_long_appends(monkeypatch, value_bits):
     o_gpu, _ = gpu_decode(run, q)
     o_ref = tq.decode(run.P, gc, q.double().numpy(), np.arange(2), run.lens)
     assert decode_error(o_gpu, o_ref) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("wname,max_new", [("hd256_long_dense_3_2", 1), ("gqa_decode", 32), ("outlier_stress", 40)])
+def test_understated_launch_bound_still_writes_every_token(wname, max_new):
+    """max_new_per_seq only sizes the launch: 200- and 130-token appends with a
+    bound of 1 (dense matrix-core kernel, two chunk workers per sequence) or 32
+    and 40 (token-per-lane kernel) must still write every position."""
+    w = workloads.WORKLOADS[wname]
+    w = w.replace(num_q_heads=w.num_q_heads // w.num_kv_heads * 2, num_kv_heads=2)
+    print(f"[parity] understated bound {wname} max_new={max_new}", flush=True)
+    run = make_run(w, [200, 130], max_new=max_new)
+    rep = compare_append(run)
+    print(f"[parity] {rep}", flush=True)
+    assert rep.tokens == 330 * 2 and rep.unexcused == 0 and rep.window_mismatch == 0
+    assert rep.max_nu_rel < NORM_RTOL and rep.max_gamma_rel < NORM_RTOL
+
+
+@pytest.mark.parametrize("wname", ["gqa_decode", "hd256_long_dense_3_2"])
+def test_status_word_reports_skipped_work(wname):
+    """Debug capacity checks: a block-table entry outside the pool, a slot
+    outside the table and a position beyond the table's pages are skipped and
+    reported in the caller's status word, and every other token is written
+    exactly as the oracle writes it."""
+    import kv_cache_vector_append_amd as tqa
+    from harness import lib_config, oracle_config
+    w = workloads.WORKLOADS[wname]
+    w = w.replace(num_q_heads=w.num_q_heads // w.num_kv_heads * 2, num_kv_heads=2)
+    cfg, ocfg = lib_config(w), oracle_config(w)
+    dev = "cuda"
+    lens, mpp = [300, 90], 20
+    bt = workloads.block_table(w, 2, mpp).numpy().copy()
+    bad_page = 4                                   # positions 64..79 of sequence 0, outside the window
+    bt[0, bad_page] = 2 * mpp + 7                  # outside the 2 * mpp pages of the pool
+    params = torch.empty(tqa.params_bytes(cfg), dtype=torch.uint8, device=dev)
+    tqa.init_codebooks(cfg, params)
+    cache = tqa.allocate_cache(cfg, 2 * mpp, torch.from_numpy(bt), dev)
+    cache.status = torch.zeros(1, dtype=torch.int32, device=dev)
+    K = [workloads.kv_tokens(w, "k", s, 0, n) for s, n in enumerate(lens)]
+    V = [workloads.kv_tokens(w, "v", s, 0, n) for s, n in enumerate(lens)]
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    kn, vn = torch.cat(K).to(dev), torch.cat(V).to(dev)
+    cu = [0, lens[0], lens[0] + lens[1]]
+    for max_new in (300, 8):                       # two launch shapes (and, for FWHT, two kernels)
+        cache.status.zero_()
+        tqa.quantize_append(cfg, params, cache, kn, vn, i32([0, 1]), i32([0, 0]), i32(cu), max_new)
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == tqa.TQ_STATUS_BAD_PAGE
+    # every position outside the bad page is bit-exact (up to the threshold band)
+    P = tq.Params(ocfg)
+    from harness import Run, compare_append as cmp
+    run = Run(w, lens, cfg, params, cache, ocfg, P, tq.Cache(ocfg, 2 * mpp, np.where(bt >= 2 * mpp, 0, bt)), K, V,
+              np.where(bt >= 2 * mpp, 0, bt))
+    keep = [np.array([p for p in range(lens[0]) if p // w.page_tokens != bad_page]), np.arange(lens[1])]
+    rep = cmp(run, positions=keep)
+    assert rep.tokens == (lens[0] - 16 + lens[1]) * 2 and rep.unexcused == 0
+    # a slot outside the table, and positions past the table's pages
+    cache.status.zero_()
+    tqa.quantize_append(cfg, params, cache, kn[:10], vn[:10], i32([5]), i32([0]), i32([0, 10]), 10)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == tqa.TQ_STATUS_BAD_SLOT
+    cache.status.zero_()
+    tqa.quantize_append(cfg, params, cache, kn[:40], vn[:40], i32([1]), i32([mpp * 16 - 8]), i32([0, 40]), 40)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == tqa.TQ_STATUS_CAPACITY
+    # decode over the bad page: reported, and the output stays finite
+    cache.status.zero_()
+    q = queries(w, 2)
+    o_gpu, _ = gpu_decode(run, q)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & tqa.TQ_STATUS_BAD_PAGE
+    assert np.isfinite(o_gpu).all()

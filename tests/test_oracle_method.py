@@ -197,3 +197,37 @@ def test_encode_matches_plain_definitions():
     assert np.array_equal(e["codes"], nearest)
     w = (P.T.sketch_matrix() @ (e["y"] - P.kc[nearest]).T).T
     assert np.array_equal(e["z"], w < 0)
+
+
+@pytest.mark.parametrize("d,kb,vb,rot", [(128, 3, 4, "fwht"), (256, 3, 4, "dense"), (128, 4, 2, "dense"),
+                                         (256, 4, 2, "fwht"), (128, 2, 3, "fwht")])
+def test_value_codec_distortion_and_cosine_closed_forms(d, kb, vb, rot):
+    """encode_values / dequantize_values at the configured value bits.
+
+    For a uniformly rotated unit vector every coordinate follows f_d, so the
+    per-vector squared error of the Lloyd-Max codec is D_b(d) / d per
+    coordinate on average (Thm 1 in expectation: E||u - u~||^2 = D_b), and the
+    centroid condition gives E cos(v, v~) = sqrt(1 - D_b) to first order
+    (0.9402 at 2 bits and head_dim 256, the [README] "TQ Quantization
+    Quality" value).  The key codebook here has a different bit count, so a
+    key/value codebook swap or a wrong bit count fails.
+    """
+    cfg, P = _params(d, kb, vb, rot)
+    g = np.random.default_rng(100 + d + vb)
+    n = 6000
+    x = g.standard_normal((n, d)) * g.uniform(0.5, 3.0, (n, 1))
+    ev = tq.encode_values(P, x)
+    assert ev["codes"].max() == (1 << vb) - 1 and ev["codes"].min() == 0
+    assert np.allclose(ev["nu"], np.linalg.norm(x, axis=1), rtol=1e-15)
+    vt = tq.dequantize_values(P, ev["codes"], ev["nu"])
+    D = codebook.distortion(codebook.lloyd_max(d, vb), d)
+    Dk = codebook.distortion(codebook.lloyd_max(d, kb - 1), d)
+    err = ((x - vt) ** 2).sum(1) / ev["nu"] ** 2
+    se = err.std() / np.sqrt(n)
+    assert abs(err.mean() - D) < 5 * se, (err.mean(), D)
+    assert abs(err.mean() - Dk) > 20 * se          # distinguishable from the key codebook
+    cos = (x * vt).sum(1) / np.linalg.norm(x, axis=1) / np.linalg.norm(vt, axis=1)
+    # first order in D (Jensen's gap is O(Var D)): allow 2% of D on top of the sampling error
+    assert abs(cos.mean() - np.sqrt(1 - D)) < 5 * cos.std() / np.sqrt(n) + 0.02 * D
+    if d == 256 and vb == 2:
+        assert abs(cos.mean() - README["value_cos_2bit_head_dim256"]) < 2e-3
