@@ -487,7 +487,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   constexpr int NKT = (1 << (MK - 1)) - 1 > 0 ? (1 << (MK - 1)) - 1 : 1, NKC = 1 << (MK - 1);
   constexpr int NVT = (1 << (BV - 1)) - 1 > 0 ? (1 << (BV - 1)) - 1 : 1;
   constexpr int KWORDS = NG * (MK + 1);
-  const int lane = threadIdx.x;
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads, W = cv.window;
   int unit = blockIdx.x;
@@ -509,6 +508,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
   // chunks chunk, chunk + parts, ...: every 64-position chunk of the new
   // tokens is written whatever max_new_per_seq the launch was sized with
   for (int P0 = (start / 64 + chunk) * 64; P0 < new_len; P0 += a.parts * 64) {
+    // lane-derived values are recomputed in every chunk (hoisted out of the
+    // loop they would stay live in registers across the whole body)
+    int lane = threadIdx.x;
+    asm volatile("" : "+v"(lane));
     const int pos = P0 + lane;
     const bool valid = pos >= start && pos < new_len;
     const int g = lane >> 4, t = lane & 15;
@@ -532,9 +535,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ap
     const bool in_window = valid && W > 0 && pos >= new_len - W;
     const size_t row = (size_t(b0) + (pos - start)) * H + h;
 
-    const const_f32* prm = (const const_f32*)a.params;
+    // the parameters are re-addressed in every chunk: hoisting their loads out
+    // of the chunk loop would hold them (dense: the matrix operands) in
+    // registers across the whole body
+    const uint8_t* params = a.params;
+    asm volatile("" : "+s"(params));
+    const const_f32* prm = (const const_f32*)params;
     // the four sign vectors (roles KR, KS1, KS2, VR), read through the scalar cache
-    const const_u32* sgn_words = (const const_u32*)(a.params + kOffSigns);
+    const const_u32* sgn_words = (const const_u32*)(params + kOffSigns);
     auto sgn = [&](int role) { return sgn_words + role * (kSignRoleBytes / 4); };
     const float sqd = sqrtf(float(D));
     const size_t plane_bytes = size_t(P) * D / 8;
@@ -861,7 +869,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   constexpr int KWORDS = (D / 32) * (MK + 1);
   __shared__ __attribute__((aligned(16))) uint8_t buf[T * DT::ROWB];
   __shared__ float nrm[T], esum[4][T];
-  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads, W = cv.window;
   int unit = blockIdx.x;
@@ -883,6 +890,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // chunks chunk, chunk + parts, ... (uniform per workgroup): every chunk of
   // the new tokens is written whatever max_new_per_seq the launch was sized with
   for (int P0 = (start / T + chunk) * T; P0 < new_len; P0 += a.parts * T) {
+    // thread-derived values are recomputed in every chunk (hoisted out of the
+    // loop they would stay live in registers across the whole body)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, q = tid >> 6;
     const const_i32* bt = (const const_i32*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
     int phys[4];
 #pragma unroll
@@ -893,8 +905,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       if (cv.status != nullptr && lane == 0 && pg * P < new_len && (pg + 1) * P > start && phys[j] < 0)
         report(cv.status, true, pg < cv.max_pages_per_seq ? TQ_STATUS_BAD_PAGE : TQ_STATUS_CAPACITY);
     }
-    const const_f32* prm = (const const_f32*)a.params;
-    const _Float16* m16 = reinterpret_cast<const _Float16*>(a.params + dense16_offset(D, 0));
+    // the parameters are re-addressed in every chunk: hoisting their loads out
+    // of the chunk loop would hold them (dense: the matrix operands) in
+    // registers across the whole body
+    const uint8_t* params = a.params;
+    asm volatile("" : "+s"(params));
+    const const_f32* prm = (const const_f32*)params;
+    const _Float16* m16 = reinterpret_cast<const _Float16*>(params + dense16_offset(D, 0));
     const size_t mm = size_t(D) * D;  // halves per fp16 matrix
     const size_t plane_bytes = size_t(P) * D / 8;
 

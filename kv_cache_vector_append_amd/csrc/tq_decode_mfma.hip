@@ -163,6 +163,29 @@ __device__ __forceinline__ void block_sync() {
   lds_fence();
 }
 
+// ---------------------------------------------------------------------------- debug capacity checks
+// Reports, in the caller's status word, a slot outside the table, a length
+// the call clamps, and every block-table entry outside the pool among the
+// pages the compressed part of sequence s reads.  Run by the query-preparation
+// workgroup of the sequence's first kv head, and only when a status word was
+// given, so the split kernel carries no bookkeeping.
+__device__ void check_sequence(const DecodeArgs& a, int s, int tid, int nthreads) {
+  const CacheView& cv = a.cache;
+  const int slot = a.seq_slots[s];
+  const int L = a.ctx_len[s];
+  const bool slot_ok = slot >= 0 && slot < cv.max_seqs;
+  if (tid == 0) {
+    report(cv.status, !slot_ok, TQ_STATUS_BAD_SLOT);
+    report(cv.status, L < 0 || L > min(cv.max_pages_per_seq * kPage, a.max_ctx), TQ_STATUS_CAPACITY);
+  }
+  if (!slot_ok) return;
+  const int Lc = max(0, min(L, min(cv.max_pages_per_seq * kPage, a.max_ctx)));
+  const int nc = cv.window > 0 ? max(0, Lc - cv.window) : Lc;
+  const int32_t* bt = cv.block_table + size_t(slot) * cv.max_pages_per_seq;
+  for (int pg = tid; pg * kPage < nc; pg += nthreads) report(cv.status, uint32_t(bt[pg]) >= uint32_t(cv.num_pages),
+                                                            TQ_STATUS_BAD_PAGE);
+}
+
 // ---------------------------------------------------------------------------- query operands
 // One workgroup per (sequence, kv head); wavefront h rotates and sketches query
 // head h of the GQA group in registers (FWHT variant) and reduces its operand
@@ -181,6 +204,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   const int G = a.num_q_heads / H;
   const int s = blockIdx.x / H, hk = blockIdx.x % H;
   uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK);
+  if (a.cache.status != nullptr && hk == 0) check_sequence(a, s, tid, T);
   // scores come out in base-2 logits: the softmax scale times log2(e) rides on
   // both query operands, and the QJL constant sqrt(pi/2)/d on the sketch one
   const float s2 = a.scale * 1.4426950408889634f;
@@ -621,10 +645,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 
   const int slot = a.seq_slots[s];
   int L = a.ctx_len[s];
-  if (cv.status != nullptr && split == 0 && tid == 0) {
-    report(cv.status, slot < 0 || slot >= cv.max_seqs, TQ_STATUS_BAD_SLOT);
-    report(cv.status, L < 0 || L > min(cv.max_pages_per_seq * kPage, a.max_ctx), TQ_STATUS_CAPACITY);
-  }
   if (slot < 0 || slot >= cv.max_seqs || L < 0) L = 0;
   if (L > cv.max_pages_per_seq * kPage) L = cv.max_pages_per_seq * kPage;
   if (L > a.max_ctx) L = a.max_ctx;
@@ -831,7 +851,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       const float qsum = (dq[j][0] + dq[j][1]) + (dq[j][2] + dq[j][3]);
       const float est = knj.x * fmaf(knj.y, qsum, msum);
       const bool tok_ok = pos < t_end && kok[j];
-      if (cv.status != nullptr) report(cv.status, pos < t_end && !kok[j], TQ_STATUS_BAD_PAGE);
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? est : -INFINITY;
       vnu[j] = tok_ok ? vnj : 0.f;
