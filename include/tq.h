@@ -192,6 +192,28 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
                               float softmax_scale, float* out, void* workspace,
                               size_t workspace_bytes, float* logits_or_null, void* stream);
 
+/* Bytes of the library-owned decode workspace tq_decode_attention_static
+ * uses (one copy per GPU, held until the process ends). */
+#define TQ_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/* tq_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results and errors as
+ * tq_decode_attention, except that the workspace is a library-owned device
+ * array of TQ_STATIC_WORKSPACE_BYTES per GPU: calls whose
+ * tq_decode_workspace_bytes(cfg, num_seqs, max_ctx) exceeds it return
+ * TQ_ERR_CAPACITY before anything is enqueued.  Allocates and frees nothing.
+ * All calls on one GPU share that array (each call writes every part of it
+ * it reads, so nothing needs clearing), so calls that overlap on one GPU --
+ * on different streams, or from different threads -- race and must not be
+ * issued.  The array's address on the current GPU is looked up on the first
+ * call there (tq_init_codebooks does it too, so that a caller that captures
+ * the call in a graph can resolve it beforehand). */
+tq_status tq_decode_attention_static(const tq_config* cfg, const void* params_dev, const tq_cache* cache,
+                                     const void* q, tq_dtype q_dtype, const int32_t* seq_slots,
+                                     const int32_t* ctx_len, int32_t num_seqs, int32_t max_ctx,
+                                     float softmax_scale, float* out, float* logits_or_null, void* stream);
+
 /* Reconstruct the page-resident keys and values of positions
  * [tok_begin, tok_end) of cache row seq_slot ([Reconstruction] "Step 5":
  * centroid lookup, inverse rotation, scaling by the stored norm; keys also add

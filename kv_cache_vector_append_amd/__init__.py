@@ -7,6 +7,7 @@ from ._lib import (  # noqa: F401
     CacheBuffers,
     Config,
     TQ_MAX_CONTEXT,
+    TQ_STATIC_WORKSPACE_BYTES,
     TQ_STATUS_BAD_PAGE,
     TQ_STATUS_BAD_SLOT,
     TQ_STATUS_CAPACITY,
@@ -14,6 +15,7 @@ from ._lib import (  # noqa: F401
     allocate_cache,
     build_id,
     decode_attention,
+    decode_attention_static,
     decode_workspace_bytes,
     dequantize,
     exported_symbols,

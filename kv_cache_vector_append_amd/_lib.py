@@ -61,6 +61,7 @@ def load_library() -> ctypes.CDLL:
         "tq_quantize_append": (I32, [cfgp, P, cachep, P, P, I32, P, P, P, I32, I32, I32, P]),
         "tq_decode_workspace_bytes": (SZ, [cfgp, I32, I32]),
         "tq_decode_attention": (I32, [cfgp, P, cachep, P, I32, P, P, I32, I32, F32, P, P, SZ, P, P]),
+        "tq_decode_attention_static": (I32, [cfgp, P, cachep, P, I32, P, P, I32, I32, F32, P, P, P]),
         "tq_dequantize": (I32, [cfgp, P, cachep, I32, I32, I32, P, P, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
@@ -76,7 +77,8 @@ def load_library() -> ctypes.CDLL:
 
 def exported_symbols():
     return ["tq_params_bytes", "tq_key_block_bytes", "tq_value_block_bytes", "tq_init_codebooks",
-            "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_dequantize",
+            "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_static",
+            "tq_dequantize",
             "tq_status_string", "tq_last_error", "tq_build_id"]
 
 
@@ -119,6 +121,7 @@ class Config:
 
 TQ_STATUS_BAD_SLOT, TQ_STATUS_BAD_PAGE, TQ_STATUS_CAPACITY = 1, 2, 4
 TQ_MAX_CONTEXT = 1 << 30
+TQ_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
 def build_id() -> str:
@@ -195,6 +198,16 @@ def decode_attention(cfg: Config, params_dev, cache: CacheBuffers, q, seq_slots,
         ctypes.byref(cfg.c()), _ptr(params_dev), ctypes.byref(cc), _ptr(q), _DTYPE[q.dtype], _ptr(seq_slots),
         _ptr(ctx_len), int(q.shape[0]), int(max_ctx), float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(logits), _stream(stream)), "tq_decode_attention")
+
+
+def decode_attention_static(cfg: Config, params_dev, cache: CacheBuffers, q, seq_slots, ctx_len, max_ctx: int, out,
+                            scale: float = 0.0, logits=None, stream=None):
+    """decode_attention with the library-owned workspace (no allocation anywhere)."""
+    cc = cache.c()
+    _check(load_library().tq_decode_attention_static(
+        ctypes.byref(cfg.c()), _ptr(params_dev), ctypes.byref(cc), _ptr(q), _DTYPE[q.dtype], _ptr(seq_slots),
+        _ptr(ctx_len), int(q.shape[0]), int(max_ctx), float(scale), _ptr(out), _ptr(logits), _stream(stream)),
+        "tq_decode_attention_static")
 
 
 def dequantize(cfg: Config, params_dev, cache: CacheBuffers, seq_slot: int, tok_begin: int, tok_end: int,

@@ -123,6 +123,10 @@ tq_status tq_init_codebooks(const tq_config* cfg, void* params_dev, void* params
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(params)");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  // resolve this GPU's library-owned decode workspace now, outside any graph capture
+  void* ws = nullptr;
+  const int we = tqi::static_workspace(&ws);
+  if (we != 0) return hip_fail(we, "library-owned workspace lookup");
   return TQ_OK;
 }
 
@@ -170,10 +174,16 @@ size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t
   return tqi::decode_prep_bytes(cfg->head_dim, num_seqs, cfg->num_kv_heads) + partials;
 }
 
-tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, const tq_cache* cache, const void* q,
-                              tq_dtype q_dtype, const int32_t* seq_slots, const int32_t* ctx_len,
-                              int32_t num_seqs, int32_t max_ctx, float softmax_scale, float* out,
-                              void* workspace, size_t workspace_bytes, float* logits_or_null, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by tq_decode_attention and
+// tq_decode_attention_static; `workspace` NULL selects the library-owned one.
+tq_status decode(const tq_config* cfg, const void* params_dev, const tq_cache* cache, const void* q,
+                 tq_dtype q_dtype, const int32_t* seq_slots, const int32_t* ctx_len, int32_t num_seqs,
+                 int32_t max_ctx, float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                 float* logits_or_null, void* stream, bool library_workspace) {
   tq_status st = check_config(cfg);
   if (st != TQ_OK) return st;
   if ((st = check_cache(cfg, cache)) != TQ_OK) return st;
@@ -182,12 +192,22 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
   if (num_seqs < 0 || max_ctx < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "negative sizes");
   if (max_ctx > TQ_MAX_CONTEXT) return fail(TQ_ERR_CAPACITY, "max_ctx %d above %d", max_ctx, TQ_MAX_CONTEXT);
   if (num_seqs == 0) return TQ_OK;
-  if (!q || !seq_slots || !ctx_len || !out || !workspace) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned4(seq_slots) || !aligned4(ctx_len))
+  if (!q || !seq_slots || !ctx_len || !out || (!library_workspace && !workspace))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned16(q) || !aligned16(out) || (!library_workspace && !aligned16(workspace)) || !aligned4(seq_slots) ||
+      !aligned4(ctx_len))
     return fail(TQ_ERR_INVALID_ARGUMENT, "pointers misaligned");
   if (logits_or_null && !aligned4(logits_or_null)) return fail(TQ_ERR_INVALID_ARGUMENT, "logits misaligned");
   const int mc = max_ctx > 0 ? max_ctx : 1;
   const size_t need = tq_decode_workspace_bytes(cfg, num_seqs, mc);
+  if (library_workspace) {
+    if (need > TQ_STATIC_WORKSPACE_BYTES)
+      return fail(TQ_ERR_CAPACITY, "decode needs %zu workspace bytes, above the library-owned %u", need,
+                  unsigned(TQ_STATIC_WORKSPACE_BYTES));
+    const int e = tqi::static_workspace(&workspace);
+    if (e != 0) return hip_fail(e, "library-owned workspace lookup");
+    workspace_bytes = TQ_STATIC_WORKSPACE_BYTES;
+  }
   if (workspace_bytes < need)
     return fail(TQ_ERR_CAPACITY, "workspace %zu bytes < %zu required", workspace_bytes, need);
   const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, mc);
@@ -213,6 +233,26 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, cons
                                                  : tqi::launch_decode(*cfg, a, stream);
   if (e != 0) return hip_fail(e, "decode launch");
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_attention(const tq_config* cfg, const void* params_dev, const tq_cache* cache, const void* q,
+                              tq_dtype q_dtype, const int32_t* seq_slots, const int32_t* ctx_len,
+                              int32_t num_seqs, int32_t max_ctx, float softmax_scale, float* out,
+                              void* workspace, size_t workspace_bytes, float* logits_or_null, void* stream) {
+  return decode(cfg, params_dev, cache, q, q_dtype, seq_slots, ctx_len, num_seqs, max_ctx, softmax_scale, out,
+                workspace, workspace_bytes, logits_or_null, stream, false);
+}
+
+tq_status tq_decode_attention_static(const tq_config* cfg, const void* params_dev, const tq_cache* cache,
+                                     const void* q, tq_dtype q_dtype, const int32_t* seq_slots,
+                                     const int32_t* ctx_len, int32_t num_seqs, int32_t max_ctx,
+                                     float softmax_scale, float* out, float* logits_or_null, void* stream) {
+  return decode(cfg, params_dev, cache, q, q_dtype, seq_slots, ctx_len, num_seqs, max_ctx, softmax_scale, out,
+                nullptr, 0, logits_or_null, stream, true);
 }
 
 tq_status tq_dequantize(const tq_config* cfg, const void* params_dev, const tq_cache* cache, int32_t seq_slot,

@@ -138,4 +138,8 @@ size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-opera
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);
 
+// Device address of the current GPU's library-owned decode workspace of
+// TQ_STATIC_WORKSPACE_BYTES (tq_scratch.hip); returns hipError_t as int.
+int static_workspace(void** ptr);
+
 }  // namespace tqi
