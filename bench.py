@@ -11,8 +11,11 @@ HBM before timing starts.  Prints one JSON line.
 value = decoded cached tokens per second over the whole step (sum of context
 lengths attended per step / step time).  The `roofline` object covers the
 dominant call, timed live with HIP events on the stream the library launches
-on; `cpu_baseline` times the float64 oracle on a bounded sample of the same
-workload on the host.
+on; `quality_vs_exact` compares one head's output and logit ranking with exact
+attention over its raw keys and values; `other_workloads` repeats the step for
+the other workloads (mixed serving, head_dim 256 at both bit widths, the dense
+append, GQA decode); `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload on the host's cores (before the GPU is used).
 """
 from __future__ import annotations
 
@@ -202,9 +205,11 @@ class Setup:
     pass
 
 
-def build_decode_setup(w, tqa, torch, dev):
+def build_decode_setup(w, tqa, torch, dev, keep_head=None):
     """Cache filled with decode_ctx - 1 tokens per sequence; the step appends token
-    decode_ctx - 1 of every sequence and decodes over decode_ctx tokens."""
+    decode_ctx - 1 of every sequence and decodes over decode_ctx tokens.
+    keep_head = (seq, kv head): also keep that head's raw keys and values of all
+    decode_ctx positions on the device (S.head_k, S.head_v), for quality metrics."""
     import workloads
     S = Setup()
     nseq, ctx = w.decode_seqs, w.decode_ctx
@@ -219,17 +224,27 @@ def build_decode_setup(w, tqa, torch, dev):
     i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
     slots = i32(list(range(nseq)))
     chunk = 16384
+    hk_parts, hv_parts = [], []
     for start in range(0, ctx - 1, chunk):
         n = min(chunk, ctx - 1 - start)
         k = workloads.device_kv(w, "k", nseq * n, g, dev)
         v = workloads.device_kv(w, "v", nseq * n, g, dev)
         tqa.quantize_append(S.cfg, S.params, S.cache, k, v, slots, i32([start] * nseq),
                             i32([i * n for i in range(nseq + 1)]), n)
+        if keep_head is not None:
+            hs, hh = keep_head
+            hk_parts.append(k[hs * n:(hs + 1) * n, hh].clone())
+            hv_parts.append(v[hs * n:(hs + 1) * n, hh].clone())
         del k, v
     torch.cuda.synchronize()
     log(f"prefilled {nseq} x {ctx - 1} tokens")
     S.step_k = workloads.device_kv(w, "k", nseq, g, dev)
     S.step_v = workloads.device_kv(w, "v", nseq, g, dev)
+    if keep_head is not None:
+        hs, hh = keep_head
+        S.keep_head = keep_head
+        S.head_k = torch.cat(hk_parts + [S.step_k[hs:hs + 1, hh]])
+        S.head_v = torch.cat(hv_parts + [S.step_v[hs:hs + 1, hh]])
     S.app_args = (slots, i32([ctx - 1] * nseq), i32(list(range(nseq + 1))), 1)
     S.q = workloads.device_queries(w, nseq, g, dev)
     S.dec_slots, S.dec_lens = slots, i32([ctx] * nseq)
@@ -290,12 +305,13 @@ def replicate_cache(S, tqa, w, copies):
                       for _ in range(copies - 1)]
 
 
-def run_gpu(w, steps, warmup, copies):
+def run_gpu(w, steps, warmup, copies, keep_head=None):
     import torch
     import kv_cache_vector_append_amd as tqa
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    S = build_mixed_setup(w, tqa, torch, dev) if w.prefill_seqs else build_decode_setup(w, tqa, torch, dev)
+    S = (build_mixed_setup(w, tqa, torch, dev) if w.prefill_seqs
+         else build_decode_setup(w, tqa, torch, dev, keep_head=keep_head))
     if copies <= 0:
         copies = 4 if decode_algorithmic_bytes(w, S.lens) < 2 ** 30 else 1
     replicate_cache(S, tqa, w, copies)
@@ -337,55 +353,160 @@ def run_gpu(w, steps, warmup, copies):
     log(f"{steps} steps: {total_ms:.3f} ms on the stream ({wall * 1e3:.1f} ms wall); "
         f"append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us per call")
     return dict(total_ms=total_ms, app_ms=app_ms, dec_ms=dec_ms, lens=S.lens, app_counts=S.app_counts,
-                app_lens_after=S.app_lens_after, copies=copies)
+                app_lens_after=S.app_lens_after, copies=copies, setup=S)
+
+
+def step_summary(w, r, steps):
+    """Per-step throughput and each call's achieved HBM rate for one workload."""
+    ms = r["total_ms"] / steps
+    dec_bytes = decode_algorithmic_bytes(w, r["lens"])
+    app_bytes = append_algorithmic_bytes(w, r["app_counts"], r["app_lens_after"])
+    out = {"ms_per_step": round(ms, 5), "value": round(sum(r["lens"]) / (ms / 1e3), 1), "unit": "cached tokens/s"}
+    for call, b, t in (("decode", dec_bytes, r["dec_ms"]), ("append", app_bytes, r["app_ms"])):
+        gbs = b / (t / 1e3) / 1e9
+        out[call] = {"avg_launch_ms": round(t, 5), "algorithmic_bytes_per_launch": int(b),
+                     "achieved_GBs": round(gbs, 2), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if w.rotation == "dense" and w.prefill_seqs:
+        tflops = dense_append_flops(w, r["app_counts"]) / (r["app_ms"] / 1e3) / 1e12
+        out["append"].update({"bound": "mfma", "achieved_TFLOPs": round(tflops, 2),
+                              "frac_of_fp16_mfma_peak": round(tflops / PEAK_MFMA_F16_TFLOPS, 4)})
+    return out
+
+
+def quality_vs_exact(w, S):
+    """Output cosine, and the Spearman rank correlation and Recall@8 of the
+    logits, of one kv head's query group against exact softmax attention over
+    that head's raw keys and values (fp32 on the device: a measurement, not
+    part of the library's path)."""
+    import torch
+    import kv_cache_vector_append_amd as tqa
+    hs, hh = S.keep_head
+    G, d, L = w.gqa, w.head_dim, S.lens[hs]
+    logits = torch.full((len(S.lens), w.num_q_heads, S.max_ctx), float("nan"), device=S.q.device)
+    tqa.decode_attention(S.cfg, S.params, S.cache, S.q, S.dec_slots, S.dec_lens, S.max_ctx, S.out, S.ws,
+                         logits=logits)
+    torch.cuda.synchronize()
+    q = S.q[hs, hh * G:(hh + 1) * G].float()
+    K, V = S.head_k.float(), S.head_v.float()
+    exact_logits = (q @ K.T) / math.sqrt(d)
+    o_exact = torch.softmax(exact_logits, dim=-1) @ V
+    o = S.out[hs, hh * G:(hh + 1) * G]
+    cos = torch.nn.functional.cosine_similarity(o, o_exact, dim=-1)
+    est = logits[hs, hh * G:(hh + 1) * G, :L]
+
+    def ranks(x):
+        r = torch.empty_like(x)
+        r.scatter_(-1, torch.argsort(x, dim=-1), torch.arange(x.shape[-1], device=x.device, dtype=x.dtype).expand_as(x))
+        return r
+
+    ra, rb = ranks(est.double()), ranks(exact_logits.double())
+    ra, rb = ra - ra.mean(-1, keepdim=True), rb - rb.mean(-1, keepdim=True)
+    rho = (ra * rb).sum(-1) / (ra.norm(dim=-1) * rb.norm(dim=-1))
+    top_a = torch.topk(est, 8, dim=-1).indices
+    top_b = torch.topk(exact_logits, 8, dim=-1).indices
+    recall = (top_a[:, :, None] == top_b[:, None, :]).any(-1).float().mean(-1)
+    return {"against": "exact fp32 softmax attention over the raw bf16 keys and values",
+            "head": f"sequence {hs}, kv head {hh}, {G} query heads, {L} tokens",
+            "cos_sim_min": round(float(cos.min()), 6), "cos_sim_mean": round(float(cos.mean()), 6),
+            "spearman_rho_mean": round(float(rho.mean()), 5), "spearman_rho_min": round(float(rho.min()), 5),
+            "recall_at_8_mean": round(float(recall.mean()), 4), "recall_at_8_min": round(float(recall.min()), 4)}
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(w, budget_s=20.0):
-    """Time the float64 oracle (as it stands) on a bounded sample of the workload
-    and scale to decoded cached tokens per second for the whole step."""
-    import torch
+# One oracle work unit: one (sequence, kv head) of the workload -- append
+# UNIT_CTX tokens of that kv head, then decode its query group over them.
+# Built in the parent before any worker is forked (and before the GPU is
+# touched); the workers only run numpy.
+UNIT_CTX = 8192
+MAX_WORKERS = 16          # the host's CPU share per GPU
+_UNIT = {}
+
+
+def _unit_setup(w):
     import workloads
     from oracle import tq
+    G = w.gqa
+    cfg1 = tq.Config(w.head_dim, G, 1, w.key_bits, w.value_bits, w.page_tokens, w.window, w.rotation,
+                     w.method_seed)
+    ctx = min(UNIT_CTX, w.decode_ctx)
+    _UNIT.update(cfg=cfg1, P=tq.Params(cfg1), ctx=ctx,
+                 K=workloads.kv_tokens(w, "k", 0, 0, ctx)[:, 0:1].double().numpy(),
+                 V=workloads.kv_tokens(w, "v", 0, 0, ctx)[:, 0:1].double().numpy(),
+                 q=workloads.queries(w, 0)[:G].double().numpy()[None])
+
+
+def _unit_run(_=None):
+    """(append seconds, decode seconds) of one unit, on one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import tq
+    u = _UNIT
+    with threadpool_limits(1):
+        mpp = math.ceil(u["ctx"] / u["cfg"].page_tokens)
+        c = tq.Cache(u["cfg"], mpp, np.arange(mpp)[None])
+        t0 = time.perf_counter()
+        tq.append(u["P"], c, u["K"], u["V"], [0], [0], [0, u["ctx"]])
+        t1 = time.perf_counter()
+        tq.decode(u["P"], c, u["q"], [0], [u["ctx"]])
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline(w, reps=4):
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    (sequence, kv head) units timed on one core, then on N worker processes
+    at once (N = the host's cores, at most MAX_WORKERS), scaled to the step's
+    appended token-heads and cached token-heads.  Call before the GPU is used
+    (the workers are forked)."""
+    import multiprocessing as mp
+    _unit_setup(w)
+    _unit_run()                                                    # warm-up
+    one = [_unit_run() for _ in range(reps)]
+    t_app = float(np.median([a for a, _ in one])) / _UNIT["ctx"]   # seconds per appended token-head
+    t_dec = float(np.median([d for _, d in one])) / _UNIT["ctx"]   # seconds per cached token-head (query group)
+    cores = os.cpu_count() or 1
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    ocfg = tq.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
-                     w.window, w.rotation, w.method_seed)
-    P = tq.Params(ocfg)
-    sample_ctx = min(w.decode_ctx, 8192)
-    mpp = math.ceil(sample_ctx / w.page_tokens)
-    cache = tq.Cache(ocfg, mpp, np.arange(mpp)[None])
-    K = workloads.kv_tokens(w, "k", 0, 0, sample_ctx).double().numpy()
-    V = workloads.kv_tokens(w, "v", 0, 0, sample_ctx).double().numpy()
-    t = time.perf_counter()
-    tq.append(P, cache, K, V, [0], [0], [0, sample_ctx])
-    t_app = time.perf_counter() - t
-    app_rate = sample_ctx / t_app                                  # tokens (all KV heads) per second
-    q = workloads.queries(w, 0).double().numpy()[None]
-    t = time.perf_counter()
-    reps = 0
-    while True:
-        tq.decode(P, cache, q, [0], [sample_ctx])
-        reps += 1
-        if time.perf_counter() - t > min(budget_s / 2, 5.0) or reps >= 20:
-            break
-    t_dec = (time.perf_counter() - t) / reps
-    dec_rate = sample_ctx / t_dec                                  # cached tokens (all heads) per second
-    step_tokens = w.decode_seqs * w.decode_ctx
-    appended = w.prefill_seqs * w.prefill_tokens if w.prefill_seqs else w.decode_seqs
-    t_step = appended / app_rate + step_tokens / dec_rate
-    return {"value": step_tokens / t_step, "unit": "cached tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle append of {sample_ctx} tokens x {w.num_kv_heads} KV heads ({t_app:.2f} s) and "
-                      f"{reps} decodes of 1 sequence x {w.num_q_heads} query heads over {sample_ctx} tokens "
-                      f"({t_dec:.2f} s each), scaled to {appended} appended tokens + {step_tokens} cached tokens "
-                      f"per step"}
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = cores
+    n = max(1, min(cores, avail, MAX_WORKERS))
+    with mp.get_context("fork").Pool(n) as pool:
+        pool.map(_unit_run, range(n))                              # warm-up in every worker
+        t0 = time.perf_counter()
+        pool.map(_unit_run, range(n * reps), chunksize=1)
+        wall = time.perf_counter() - t0
+    speedup = (n * reps / wall) * (t_app + t_dec) * _UNIT["ctx"]
+    H = w.num_kv_heads
+    cached_th = w.decode_seqs * w.decode_ctx * H
+    appended_th = (w.prefill_seqs * w.prefill_tokens if w.prefill_seqs else w.decode_seqs) * H
+    t_step_1 = appended_th * t_app + cached_th * t_dec
+    tokens = w.decode_seqs * w.decode_ctx
+    return {"value": round(tokens / (t_step_1 / speedup), 1), "unit": "cached tokens/s", "cores": n,
+            "kind": "oracle", "value_1core": round(tokens / t_step_1, 1), "speedup_over_1core": round(speedup, 2),
+            "os_cpu_count": cores,
+            "sample": f"oracle (float64 numpy, one thread per process) on (sequence, kv head) units of "
+                      f"{_UNIT['ctx']} tokens: append of the unit's tokens "
+                      f"({t_app * _UNIT['ctx']:.3f} s) and decode of its {w.gqa} query heads over them "
+                      f"({t_dec * _UNIT['ctx']:.3f} s), median of {reps} on 1 core; {n * reps} units on {n} "
+                      f"processes in {wall:.2f} s; scaled to the step's {appended_th} appended and {cached_th} "
+                      f"cached token-heads"}
 
 
 # ----------------------------------------------------------------------------- main
+
+# Workloads timed after the headline one and reported in the same line: the
+# mixed serving step (append-heavy), the head_dim-256 decode at both bit
+# widths, the dense rotation's matrix-core append, and the latency-bound GQA
+# decode.
+EXTRA_WORKLOADS = ("mixed_serving", "hd256_long_dense_3_2", "hd256_long_dense_4_4", "hd256_dense_prefill",
+                   "gqa_decode")
+# (sequence, kv head) whose query group the quality metrics cover
+QUALITY_HEAD = {"outlier_stress": (2, 5)}
+# what the decode arithmetic is: scores and value sums on the matrix cores with
+# the fp32 query / softmax weights carried as four fp8 parts against fp4 code
+# bit-planes, accumulated in fp32
+DTYPE = "fp8x4*fp4->f32"
+
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
@@ -394,6 +515,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="time only --workload")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated across steps (0: 4 when the decode working set is under 1 GiB)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "WORKLOAD"),
@@ -410,9 +532,14 @@ def main(argv=None):
         return 2
     import workloads
     w = workloads.WORKLOADS[args.workload]
+    baseline = None
+    if not args.no_cpu_baseline:
+        # first: the oracle's workers are forked, which must happen before the GPU is touched
+        log("timing the oracle on the host")
+        baseline = cpu_baseline(w)
     if args.calibrate_copy:
         calibration_copy()
-    r = run_gpu(w, args.steps, args.warmup, args.copies)
+    r = run_gpu(w, args.steps, args.warmup, args.copies, keep_head=QUALITY_HEAD.get(w.name))
     ms = r["total_ms"] / args.steps
     cached = sum(r["lens"])
     value = cached / (ms / 1e3)
@@ -441,11 +568,12 @@ def main(argv=None):
                          "hbm_achieved_GBs": round(achieved, 2)})
     other = [k for k in calls if k != dom][0]
     oc = calls[other]
+    import kv_cache_vector_append_amd as tqa
     line = {
         "metric": "decode-attn cached tokens/s over TQ-packed KV; achieved HBM GB/s % of peak",
         "value": round(value, 1), "unit": "cached tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32",
+        "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic (seeded, drawn on the device)",
         "config": {"workload": w.name, "description": w.description, "decode_seqs": w.decode_seqs,
                    "decode_ctx": w.decode_ctx, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
@@ -455,10 +583,25 @@ def main(argv=None):
         "cache_copies": r["copies"],
         f"{other}_call": {"avg_launch_ms": round(oc["ms"], 5), "algorithmic_bytes_per_launch": int(oc["bytes"]),
                           "achieved_GBs": round(oc["bytes"] / (oc["ms"] / 1e3) / 1e9, 2)},
+        "library_build_id": tqa.build_id(),
     }
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host")
-        line["cpu_baseline"] = cpu_baseline(w)
+    if w.name in QUALITY_HEAD:
+        line["quality_vs_exact"] = quality_vs_exact(w, r["setup"])
+    del r
+    if not args.no_extra:
+        import torch
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            if name == w.name:
+                continue
+            torch.cuda.empty_cache()
+            ew = workloads.WORKLOADS[name]
+            er = run_gpu(ew, 10, 3, 0)
+            extra[name] = step_summary(ew, er, 10)
+            del er
+        line["other_workloads"] = extra
+    if baseline is not None:
+        line["cpu_baseline"] = baseline
     print(json.dumps(line), flush=True)
     return 0
 

@@ -53,6 +53,8 @@ def lloyd_max(d: int, bits: int, rtol: float = 1e-13, max_iter: int = 20000):
     midpoint) until the largest centroid move is below rtol * max|c|.
     """
     L = 1 << bits
+    if L == 1:
+        return np.zeros(1)      # no code bits: the single centroid is the mean, 0
     a = (d - 1) / 2.0
     # start from equal-mass cells
     q = special.betaincinv(a, a, np.arange(1, L) / L) * 2.0 - 1.0

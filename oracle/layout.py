@@ -24,16 +24,52 @@ Value block, b = value_bits:
 
 A QJL bit is 1 where the projected residual is negative (sign bit convention).
 Slots beyond a sequence's length hold unspecified bytes.
+
+Extended formats (see tq.py): the code planes of a 32-coordinate key group,
+or of a value coordinate pair, number the bits of that coordinate's half (a
+mixed-channel rate gives the upper half d/2 .. d-1 its own count); the scaled
+key modes have no QJL plane and store (nu, s) in place of (nu, gamma); the
+key outlier sidecar adds, per token after the norms, a record of
+[count u8][index u8 x k][pad to even][fp16 value x k][pad to 4];
+group-quantized values store, after the code words, per token and
+32-coordinate group an (fp16 scale, fp16 zero) pair in place of nu.
+
+The functions take `fmt`, any object with the format attributes of
+tq.Config: head_dim, page_tokens, key_mse_bits, key_mse_bits_hi, qjl,
+key_outliers, value_bits, value_bits_hi_, value_mode.
 """
 import numpy as np
 
-
-def key_block_bytes(d: int, key_bits: int, P: int = 16) -> int:
-    return key_bits * P * d // 8 + 8 * P
+GROUP = 32
 
 
-def value_block_bytes(d: int, value_bits: int, P: int = 16) -> int:
-    return value_bits * P * d // 8 + 4 * P
+def _key_plane_counts(fmt):
+    """Planes per 32-coordinate key group (code bits, plus the QJL plane)."""
+    ng = fmt.head_dim // 32
+    q = 1 if fmt.qjl else 0
+    return [(fmt.key_mse_bits if g < ng // 2 or ng == 1 else fmt.key_mse_bits_hi) + q for g in range(ng)]
+
+
+def _value_plane_counts(fmt):
+    """Planes per value coordinate pair."""
+    npair = fmt.head_dim // 2
+    return [fmt.value_bits if i < npair // 2 else fmt.value_bits_hi_ for i in range(npair)]
+
+
+def sidecar_bytes(k: int) -> int:
+    if k == 0:
+        return 0
+    head = 1 + k + ((1 + k) & 1)
+    return (head + 2 * k + 3) // 4 * 4
+
+
+def key_block_bytes(fmt, P: int = 16) -> int:
+    return 4 * P * sum(_key_plane_counts(fmt)) + 8 * P + P * sidecar_bytes(fmt.key_outliers)
+
+
+def value_block_bytes(fmt, P: int = 16) -> int:
+    tail = P * (fmt.head_dim // GROUP) * 4 if fmt.value_mode == "group" else 4 * P
+    return 4 * sum(_value_plane_counts(fmt)) + tail
 
 
 def _bits_to_words(bits):
@@ -49,64 +85,118 @@ def _words_to_bits(w):
     return ((w[..., None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
 
 
-def pack_key_block(codes, z, nu, gamma, mse_bits: int):
-    """codes [..., P, d] ints in [0, 2^m), z [..., P, d] bool, nu/gamma [..., P] -> uint8 [..., bytes]."""
+def pack_key_block(fmt, codes, z, nu, gamma, side_idx=None, side_val=None, side_cnt=None):
+    """codes [..., P, d] ints, z [..., P, d] bool, nu/gamma [..., P], sidecar
+    [..., P, k] -> uint8 [..., key_block_bytes]."""
     codes = np.asarray(codes, dtype=np.int64)
     lead, (P, d) = codes.shape[:-2], codes.shape[-2:]
-    m = mse_bits
-    planes = [(codes >> j) & 1 for j in range(m)] + [np.asarray(z, dtype=np.int64)]
-    # [..., P, d] -> [..., P, d/32, 32] -> words [..., P, d/32]
-    words = np.stack([_bits_to_words(pl.reshape(lead + (P, d // 32, 32))) for pl in planes], axis=-1)
-    code_bytes = words.astype("<u4").view(np.uint8).reshape(lead + (P * (d // 32) * (m + 1) * 4,))
+    counts = _key_plane_counts(fmt)
+    q = 1 if fmt.qjl else 0
+    zz = np.asarray(z, dtype=np.int64)
+    words = []
+    for g, npl in enumerate(counts):
+        cg = codes[..., 32 * g:32 * (g + 1)]
+        for j in range(npl - q):
+            words.append(_bits_to_words((cg >> j) & 1))
+        if q:
+            words.append(_bits_to_words(zz[..., 32 * g:32 * (g + 1)]))
+    code_bytes = np.stack(words, axis=-1).astype("<u4").view(np.uint8).reshape(lead + (P * sum(counts) * 4,))
     norms = np.stack([np.asarray(nu, dtype="<f4"), np.asarray(gamma, dtype="<f4")], axis=-1)
-    norm_bytes = norms.view(np.uint8).reshape(lead + (8 * P,))
-    return np.concatenate([code_bytes, norm_bytes], axis=-1)
+    parts = [code_bytes, norms.view(np.uint8).reshape(lead + (8 * P,))]
+    k = fmt.key_outliers
+    if k:
+        sb = sidecar_bytes(k)
+        rec = np.zeros(lead + (P, sb), np.uint8)
+        rec[..., 0] = np.asarray(side_cnt, np.uint8)
+        rec[..., 1:1 + k] = np.asarray(side_idx, np.uint8)
+        voff = 1 + k + ((1 + k) & 1)
+        rec[..., voff:voff + 2 * k] = np.ascontiguousarray(np.asarray(side_val, "<f2")).view(np.uint8).reshape(
+            lead + (P, 2 * k))
+        parts.append(rec.reshape(lead + (P * sb,)))
+    return np.concatenate(parts, axis=-1)
 
 
-def unpack_key_block(buf, d: int, mse_bits: int, P: int = 16):
-    """Inverse of pack_key_block: returns codes [..., P, d] int64, z bool, nu f32, gamma f32."""
+def unpack_key_block(fmt, buf):
+    """Inverse of pack_key_block: codes [..., P, d] int64, z bool, nu f32, gamma f32,
+    side_idx u8 [..., P, k], side_val f16, side_cnt u8."""
     buf = np.asarray(buf, dtype=np.uint8)
     lead = buf.shape[:-1]
-    m = mse_bits
-    nbytes = P * (d // 32) * (m + 1) * 4
-    words = np.ascontiguousarray(buf[..., :nbytes]).view("<u4").reshape(lead + (P, d // 32, m + 1))
-    bits = _words_to_bits(words)                       # [..., P, d/32, m+1, 32]
-    bits = np.moveaxis(bits, -2, 0)                    # [m+1, ..., P, d/32, 32]
-    bits = bits.reshape((m + 1,) + lead + (P, d))
+    P, d = fmt.page_tokens, fmt.head_dim
+    counts = _key_plane_counts(fmt)
+    q = 1 if fmt.qjl else 0
+    nw = sum(counts)
+    words = np.ascontiguousarray(buf[..., :P * nw * 4]).view("<u4").reshape(lead + (P, nw))
     codes = np.zeros(lead + (P, d), dtype=np.int64)
-    for j in range(m):
-        codes |= bits[j].astype(np.int64) << j
-    z = bits[m].astype(bool)
-    norms = np.ascontiguousarray(buf[..., nbytes:nbytes + 8 * P]).view("<f4").reshape(lead + (P, 2))
-    return codes, z, norms[..., 0].copy(), norms[..., 1].copy()
+    z = np.zeros(lead + (P, d), dtype=bool)
+    off = 0
+    for g, npl in enumerate(counts):
+        for j in range(npl - q):
+            codes[..., 32 * g:32 * (g + 1)] |= _words_to_bits(words[..., off + j]).astype(np.int64) << j
+        if q:
+            z[..., 32 * g:32 * (g + 1)] = _words_to_bits(words[..., off + npl - 1]).astype(bool)
+        off += npl
+    nb = P * nw * 4
+    norms = np.ascontiguousarray(buf[..., nb:nb + 8 * P]).view("<f4").reshape(lead + (P, 2))
+    k = fmt.key_outliers
+    side_idx = np.zeros(lead + (P, k), np.uint8)
+    side_val = np.zeros(lead + (P, k), np.float16)
+    side_cnt = np.zeros(lead + (P,), np.uint8)
+    if k:
+        sb = sidecar_bytes(k)
+        rec = np.ascontiguousarray(buf[..., nb + 8 * P:nb + 8 * P + P * sb]).reshape(lead + (P, sb))
+        side_cnt = rec[..., 0].copy()
+        side_idx = rec[..., 1:1 + k].copy()
+        voff = 1 + k + ((1 + k) & 1)
+        side_val = np.ascontiguousarray(rec[..., voff:voff + 2 * k]).view("<f2").reshape(lead + (P, k)).copy()
+    return codes, z, norms[..., 0].copy(), norms[..., 1].copy(), side_idx, side_val, side_cnt
 
 
-def pack_value_block(codes, nu, bits: int):
+def pack_value_block(fmt, codes, nu, scale=None, zero=None):
     codes = np.asarray(codes, dtype=np.int64)
     lead, (P, d) = codes.shape[:-2], codes.shape[-2:]
     assert P == 16, "value masks pack 16 token slots per coordinate"
-    out = np.zeros(lead + (d // 2, bits), dtype=np.uint32)
     slots = np.arange(P, dtype=np.uint64)
-    for j in range(bits):
-        plane = ((codes >> j) & 1).astype(np.uint64)          # [..., P, d]
-        masks = (plane << slots[:, None]).sum(axis=-2)        # [..., d] 16-bit masks
-        masks = masks.reshape(lead + (d // 2, 2))
-        out[..., j] = (masks[..., 0] | (masks[..., 1] << np.uint64(16))).astype(np.uint32)
-    code_bytes = out.astype("<u4").view(np.uint8).reshape(lead + (d * bits * 2,))
-    nu_bytes = np.asarray(nu, dtype="<f4").view(np.uint8).reshape(lead + (4 * P,))
-    return np.concatenate([code_bytes, nu_bytes], axis=-1)
+    words = []
+    for i, b in enumerate(_value_plane_counts(fmt)):
+        for j in range(b):
+            plane = ((codes[..., 2 * i:2 * i + 2] >> j) & 1).astype(np.uint64)     # [..., P, 2]
+            masks = (plane << slots[:, None]).sum(axis=-2)                          # [..., 2]
+            words.append((masks[..., 0] | (masks[..., 1] << np.uint64(16))).astype(np.uint32))
+    code_bytes = np.stack(words, axis=-1).astype("<u4").view(np.uint8).reshape(lead + (4 * len(words),))
+    if fmt.value_mode == "group":
+        tail = np.stack([np.asarray(scale, "<f2"), np.asarray(zero, "<f2")], axis=-1)     # [..., P, d/32, 2]
+        tail = np.ascontiguousarray(tail).view(np.uint8).reshape(lead + (P * (d // GROUP) * 4,))
+    else:
+        tail = np.asarray(nu, dtype="<f4").view(np.uint8).reshape(lead + (4 * P,))
+    return np.concatenate([code_bytes, tail], axis=-1)
 
 
-def unpack_value_block(buf, d: int, bits: int, P: int = 16):
+def unpack_value_block(fmt, buf):
+    """Inverse of pack_value_block: codes [..., P, d] int64, nu f32 [..., P],
+    scale / zero f16 [..., P, d/32] (zeros in the mode that does not store them)."""
     buf = np.asarray(buf, dtype=np.uint8)
     lead = buf.shape[:-1]
-    nbytes = d * bits * 2
-    words = np.ascontiguousarray(buf[..., :nbytes]).view("<u4").reshape(lead + (d // 2, bits))
-    masks = np.stack([words & 0xFFFF, words >> 16], axis=-2)   # [..., d/2, 2, bits]
-    masks = masks.reshape(lead + (d, bits))
-    slot_bits = (masks[..., None, :] >> np.arange(P, dtype=np.uint32)[:, None]) & 1   # [..., d, P, bits]
+    P, d = fmt.page_tokens, fmt.head_dim
+    counts = _value_plane_counts(fmt)
+    nw = sum(counts)
+    words = np.ascontiguousarray(buf[..., :4 * nw]).view("<u4").reshape(lead + (nw,))
     codes = np.zeros(lead + (P, d), dtype=np.int64)
-    for j in range(bits):
-        codes |= np.swapaxes(slot_bits[..., j], -1, -2).astype(np.int64) << j
-    nu = np.ascontiguousarray(buf[..., nbytes:nbytes + 4 * P]).view("<f4").reshape(lead + (P,))
-    return codes, nu
+    slot = np.arange(P, dtype=np.uint32)
+    off = 0
+    for i, b in enumerate(counts):
+        for j in range(b):
+            w = words[..., off + j]
+            for h in range(2):
+                bits = ((w[..., None] >> (slot + np.uint32(16 * h))) & 1).astype(np.int64)      # [..., P]
+                codes[..., 2 * i + h] |= bits << j
+        off += b
+    nb = 4 * nw
+    nu = np.zeros(lead + (P,), np.float32)
+    scale = np.zeros(lead + (P, d // GROUP), np.float16)
+    zero = np.zeros(lead + (P, d // GROUP), np.float16)
+    if fmt.value_mode == "group":
+        t = np.ascontiguousarray(buf[..., nb:nb + P * (d // GROUP) * 4]).view("<f2").reshape(lead + (P, d // GROUP, 2))
+        scale, zero = t[..., 0].copy(), t[..., 1].copy()
+    else:
+        nu = np.ascontiguousarray(buf[..., nb:nb + 4 * P]).view("<f4").reshape(lead + (P,)).copy()
+    return codes, nu, scale, zero

@@ -83,8 +83,10 @@ def test_size_queries_match_layout():
     tqa = _tqa()
     for d, kb, vb, rot in CASES:
         cfg = tqa.Config(d, 8, 2, kb, vb, 16, 128, rot, 1)
-        assert tqa.key_block_bytes(cfg) == layout.key_block_bytes(d, kb)
-        assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(d, vb)
+        from oracle import tq
+        f = tq.Config(d, 8, 2, kb, vb)
+        assert tqa.key_block_bytes(cfg) == layout.key_block_bytes(f)
+        assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(f)
         assert tqa.params_bytes(cfg) == 2048 + (3 * d * d * 8 if rot == "dense" else 0)
         ws = tqa.decode_workspace_bytes(cfg, 3, 1000)
         # at least one partial record (max, denominator, d sums) per (sequence, query head)

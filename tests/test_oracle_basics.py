@@ -209,43 +209,80 @@ def test_sketch_transpose_and_row_norms(rot, d):
 
 # ---------------------------------------------------------------- layout
 
+def _fmt(d, key_bits, value_bits, **kw):
+    from oracle import tq
+    return tq.Config(d, 8, 2, key_bits, value_bits, **kw)
+
+
 def test_record_sizes_match_storage_formula():
     for case in _gold("storage_formula.json")["cases"]:
         P = 16
-        kb = layout.key_block_bytes(case["d"], case["key_bits"], P)
-        vb = layout.value_block_bytes(case["d"], case["value_bits"], P)
+        f = _fmt(case["d"], case["key_bits"], case["value_bits"])
+        kb = layout.key_block_bytes(f, P)
+        vb = layout.value_block_bytes(f, P)
         assert kb == P * case["key_record_bytes"]
         assert vb == P * case["value_record_bytes"]
         assert kb % 16 == 0 and vb % 16 == 0
 
 
-@pytest.mark.parametrize("d,m,bv", [(128, 2, 2), (128, 3, 4), (256, 2, 2), (256, 3, 3)])
-def test_pack_unpack_roundtrip(d, m, bv):
-    g = np.random.default_rng(d + m)
+def test_extended_record_sizes_match_the_bit_accounting():
+    for case in _gold("extended_formats.json")["cases"]:
+        f = _fmt(case["d"], case["key_bits"], case["value_bits"], key_mode=case["key_mode"],
+                 key_bits_hi=case["key_bits_hi"], value_bits_hi=case["value_bits_hi"],
+                 value_mode=case["value_mode"], key_outliers=case["key_outliers"])
+        assert layout.key_block_bytes(f) == 16 * case["key_record_bytes"], case["_what"]
+        assert layout.value_block_bytes(f) == 16 * case["value_record_bytes"], case["_what"]
+
+
+@pytest.mark.parametrize("d,kb,vb,kw", [(128, 3, 2, {}), (128, 4, 4, {}), (256, 3, 2, {}), (256, 4, 3, {}),
+                                        (128, 3, 2, dict(key_bits_hi=4, value_bits_hi=3)),
+                                        (64, 2, 1, dict(key_bits_hi=4, value_bits_hi=4, key_outliers=3)),
+                                        (128, 3, 2, dict(key_mode="scaled_unbiased", key_outliers=4,
+                                                         value_mode="group")),
+                                        (256, 2, 4, dict(key_mode="scaled_mse", key_bits_hi=3, value_mode="group",
+                                                         value_bits_hi=2, key_outliers=8))])
+def test_pack_unpack_roundtrip(d, kb, vb, kw):
+    from oracle import tq
+    f = _fmt(d, kb, vb, **kw)
+    g = np.random.default_rng(d + kb)
     shape = (3, 2, 16, d)
-    codes = g.integers(0, 1 << m, shape)
-    z = g.integers(0, 2, shape).astype(bool)
+    kbits = f.key_bits_of(d)
+    codes = g.integers(0, 1 << kbits, shape)
+    z = g.integers(0, 2, shape).astype(bool) & f.qjl
     nu = g.random((3, 2, 16)).astype(np.float32)
     gam = g.random((3, 2, 16)).astype(np.float32)
-    buf = layout.pack_key_block(codes, z, nu, gam, m)
-    assert buf.shape[-1] == layout.key_block_bytes(d, m + 1)
-    c2, z2, n2, g2 = layout.unpack_key_block(buf, d, m)
+    k = f.key_outliers
+    sidx = g.integers(0, d, (3, 2, 16, k)).astype(np.uint8)
+    sval = g.standard_normal((3, 2, 16, k)).astype(np.float16)
+    scnt = g.integers(0, k + 1, (3, 2, 16)).astype(np.uint8)
+    buf = layout.pack_key_block(f, codes, z, nu, gam, sidx, sval, scnt)
+    assert buf.shape[-1] == layout.key_block_bytes(f)
+    c2, z2, n2, g2, si2, sv2, sc2 = layout.unpack_key_block(f, buf)
     assert np.array_equal(c2, codes) and np.array_equal(z2, z)
     assert np.array_equal(n2, nu) and np.array_equal(g2, gam)
-    vcodes = g.integers(0, 1 << bv, shape)
-    vbuf = layout.pack_value_block(vcodes, nu, bv)
-    assert vbuf.shape[-1] == layout.value_block_bytes(d, bv)
-    vc2, vn2 = layout.unpack_value_block(vbuf, d, bv)
-    assert np.array_equal(vc2, vcodes) and np.array_equal(vn2, nu)
+    assert np.array_equal(si2, sidx) and np.array_equal(sv2.view(np.uint16), sval.view(np.uint16))
+    assert np.array_equal(sc2, scnt)
+    vcodes = g.integers(0, 1 << f.value_bits_of(d), shape)
+    vs = g.random((3, 2, 16, d // 32)).astype(np.float16)
+    vz = g.standard_normal((3, 2, 16, d // 32)).astype(np.float16)
+    vbuf = layout.pack_value_block(f, vcodes, nu, vs, vz)
+    assert vbuf.shape[-1] == layout.value_block_bytes(f)
+    vc2, vn2, vs2, vz2 = layout.unpack_value_block(f, vbuf)
+    assert np.array_equal(vc2, vcodes)
+    if f.value_mode == "group":
+        assert np.array_equal(vs2, vs) and np.array_equal(vz2, vz)
+    else:
+        assert np.array_equal(vn2, nu)
 
 
 def test_layout_bit_positions_by_hand():
     d, m = 128, 2
+    f = _fmt(d, m + 1, 2)
     codes = np.zeros((16, d), int)
     z = np.zeros((16, d), bool)
     codes[3, 37] = 2          # plane 1, token 3, coordinate 37 = group 1 bit 5
     z[5, 100] = True          # QJL plane (2), token 5, coordinate 100 = group 3 bit 4
-    buf = layout.pack_key_block(codes, z, np.zeros(16), np.zeros(16), m)
+    buf = layout.pack_key_block(f, codes, z, np.zeros(16), np.zeros(16))
     words_per_token = (d // 32) * (m + 1)
     w1 = 3 * words_per_token + 1 * (m + 1) + 1
     w2 = 5 * words_per_token + 3 * (m + 1) + 2
@@ -253,13 +290,45 @@ def test_layout_bit_positions_by_hand():
     assert buf[4 * w1] == 1 << 5 and buf[4 * w2] == 1 << 4
     nu = np.arange(16, dtype=np.float32)
     gam = -np.arange(16, dtype=np.float32)
-    buf = layout.pack_key_block(codes, z, nu, gam, m)
+    buf = layout.pack_key_block(f, codes, z, nu, gam)
     pairs = buf[16 * words_per_token * 4:].view("<f4").reshape(16, 2)
     assert np.array_equal(pairs[:, 0], nu) and np.array_equal(pairs[:, 1], gam)
     vcodes = np.zeros((16, d), int)
     vcodes[9, 70] = 3         # both planes, slot 9, coordinate 70 = low half of pair 35
     vcodes[2, 71] = 1         # plane 0, slot 2, coordinate 71 = high half of pair 35
-    vbuf = layout.pack_value_block(vcodes, np.zeros(16), 2)
+    vbuf = layout.pack_value_block(f, vcodes, np.zeros(16))
     words = vbuf[:d * 2 * 2].view("<u4").reshape(d // 2, 2)
     assert words[35, 0] == (1 << 9) | (1 << (16 + 2)) and words[35, 1] == 1 << 9
     assert np.count_nonzero(words) == 2
+
+
+def test_extended_layout_positions_by_hand():
+    """Mixed rates, scaled keys, sidecar and group scales at hand-computed offsets."""
+    d = 128
+    f = _fmt(d, 3, 2, key_mode="scaled_unbiased", key_bits_hi=4, value_bits_hi=3, key_outliers=2)
+    # key planes per group: 3, 3 (lower half), 4, 4 (upper half), no QJL plane -> 14 words per token
+    codes = np.zeros((16, d), int)
+    codes[1, 70] = 8          # plane 3 of group 2 (coordinate 70 = group 2 bit 6)
+    sidx = np.zeros((16, 2), np.uint8)
+    sval = np.zeros((16, 2), np.float16)
+    scnt = np.zeros(16, np.uint8)
+    scnt[4], sidx[4, 1], sval[4, 1] = 2, 99, np.float16(-2.5)
+    buf = layout.pack_key_block(f, codes, np.zeros((16, d), bool), np.zeros(16), np.zeros(16), sidx, sval, scnt)
+    w = 1 * 14 + (3 + 3) + 3
+    assert list(np.flatnonzero(buf[:16 * 14 * 4])) == [4 * w] and buf[4 * w] == 1 << 6
+    side = buf[16 * 14 * 4 + 16 * 8:]
+    assert len(side) == 16 * 8                 # count + 2 indices (+ pad) + 2 fp16 = 7 -> 8 bytes per token
+    rec = side[4 * 8:5 * 8]
+    assert rec[0] == 2 and rec[1] == 0 and rec[2] == 99
+    assert rec[4:8].view("<f2")[1] == np.float16(-2.5)
+    # values: pairs 0..31 carry 2 planes, pairs 32..63 carry 3
+    vcodes = np.zeros((16, d), int)
+    vcodes[7, 65] = 4         # plane 2 of pair 32 (its first pair), odd coordinate, slot 7
+    vbuf = layout.pack_value_block(f, vcodes, np.zeros(16))
+    words = vbuf[:4 * (32 * 2 + 32 * 3)].view("<u4")
+    assert list(np.flatnonzero(words)) == [32 * 2 + 2] and words[32 * 2 + 2] == 1 << (16 + 7)
+    g = _fmt(d, 3, 2, value_mode="group")
+    vbuf = layout.pack_value_block(g, np.zeros((16, d), int), None,
+                                   np.full((16, 4), 0.5, np.float16), np.full((16, 4), -1.0, np.float16))
+    tail = vbuf[4 * 64 * 2:].view("<f2").reshape(16, 4, 2)
+    assert np.all(tail[..., 0] == 0.5) and np.all(tail[..., 1] == -1.0)
