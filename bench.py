@@ -98,7 +98,7 @@ def source_hash(paths):
 # while they are unchanged) and the kernels one call launches.
 _CSRC = "kv_cache_vector_append_amd/csrc/"
 SOURCES = {
-    "decode": [_CSRC + f for f in ("tq_decode_mfma.hip", "tq_mfma.h", "tq_decode.hip", "tq_device.h",
+    "decode": [_CSRC + f for f in ("tq_decode_mfma.hip", "tq_mfma.h", "tq_codec.hip", "tq_device.h",
                                    "tq_internal.h")],
     "append": [_CSRC + f for f in ("tq_append.hip", "tq_device.h", "tq_internal.h")],
 }

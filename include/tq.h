@@ -59,34 +59,71 @@ typedef enum { TQ_ROT_FWHT = 0, TQ_ROT_DENSE = 1 } tq_rotation;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
+/* Key codec.  QJL: key_bits-1 Lloyd-Max bits plus one QJL sign bit per
+ * coordinate, score nu (<Tq, c[idx]> + gamma sqrt(pi/2)/d <STq, 1-2z>)
+ * ([Reconstruction] section 6 "The Asymmetric Unbiased Estimator").
+ * SCALED_*: all key_bits go to the Lloyd-Max code and one per-vector scale s
+ * replaces the residual bit, score s <Tq, c[idx]> ([Reconstruction] "The
+ * DRIVE/EDEN Mathematical Critique"; "12. TurboVec Additions and Divergences"
+ * item 2): UNBIASED s = nu / <y, c[idx]> (TurboVec's length renormalization,
+ * EDEN's unbiased scale), MSE s = nu <y, c[idx]> / ||c[idx]||^2 (EDEN's
+ * MSE-optimal scale). */
+typedef enum { TQ_KEY_QJL = 0, TQ_KEY_SCALED_UNBIASED = 1, TQ_KEY_SCALED_MSE = 2 } tq_key_mode;
+
+/* Value codec.  LLOYD: rotated Lloyd-Max codes and the fp32 norm.  GROUP: no
+ * rotation; per token and 32-coordinate group an fp16 scale and zero (min),
+ * uniform codes rint((v - zero) / scale) clamped to [0, 2^b - 1], decided in
+ * fp32 ([README] "How It Works" item 4; [Design Study] "Candidate key and
+ * value algorithms": the per-token value control arm). */
+typedef enum { TQ_VALUE_LLOYD = 0, TQ_VALUE_GROUP = 1 } tq_value_mode;
+
 typedef struct {
   int32_t head_dim;      /* 64, 128 or 256 */
   int32_t num_q_heads;
   int32_t num_kv_heads;  /* num_q_heads % num_kv_heads == 0 */
-  int32_t key_bits;      /* 2..4 bits per coordinate: key_bits-1 Lloyd-Max bits + 1 QJL bit
-                            ([Reconstruction] section 6 "The Residual and Bit-Splitting") */
-  int32_t value_bits;    /* 1..4 Lloyd-Max bits per coordinate, no QJL */
+  int32_t key_bits;      /* bits per key coordinate: TQ_KEY_QJL 2..4 (key_bits-1 Lloyd-Max bits
+                            + 1 QJL bit, [Reconstruction] section 6 "The Residual and
+                            Bit-Splitting"); scaled key modes 1..4 Lloyd-Max bits */
+  int32_t value_bits;    /* 1..4 bits per value coordinate, no QJL */
   int32_t page_tokens;   /* tokens per page; 16 */
   int32_t window;        /* FP16 recent-window tokens: 0 or a multiple of 16 up to 1024
                             ([Design Study] "Packed format and complete bit accounting") */
   int32_t rotation;      /* tq_rotation */
   uint64_t seed;         /* identifies the signs / matrices ([Design Study] "Paging, lifecycle,
                             and cache identity") */
+  /* Extended formats ([Design Study] "Packed format and complete bit accounting").  All zero
+     selects the default format above. */
+  int32_t key_mode;      /* tq_key_mode */
+  int32_t value_mode;    /* tq_value_mode */
+  int32_t key_bits_hi;   /* 0, or the key_bits of rotated coordinates d/2 .. d-1 (a mixed-channel
+                            rate: key_bits 3 and key_bits_hi 4 give 3.5 bits per channel) */
+  int32_t value_bits_hi; /* 0, or the value_bits of coordinates d/2 .. d-1 */
+  int32_t key_outliers;  /* 0..8 entries of the key outlier sidecar: the coordinates of largest
+                            magnitude of each key, kept as (u8 index, fp16 value) with a count
+                            byte and removed from the vector before it is quantized
+                            ([Design Study] body item 5; [Reconstruction] section 11) */
+  int32_t reserved[3];   /* zero */
 } tq_config;
 
 /* The paged cache.  Page layout per (page, KV head) block, all little-endian
  * ([Design Study] "Packed format and complete bit accounting";
  * [Reconstruction] section 8 "Bit Accounting and Memory Formulas").  Codes
- * are bit-sliced, lowest code bit first, in 32-bit words; m = key_bits - 1:
- *   key block   = for token slot t, for 32-coordinate group g, for plane j in
- *                 0..m: one word whose bit k belongs to coordinate 32g+k
- *                 (planes 0..m-1 code bits, plane m the QJL sign bits);
+ * are bit-sliced, lowest code bit first, in 32-bit words; m_g = the Lloyd-Max
+ * bits of 32-coordinate group g (key_bits - 1 in the QJL mode, key_bits in
+ * the scaled modes, from key_bits_hi for the groups of coordinates >= d/2);
+ * b_i = the value bits of coordinate pair i, likewise:
+ *   key block   = for token slot t, for group g, for plane j in 0..m_g-1: one
+ *                 word whose bit k belongs to coordinate 32g+k, then in the
+ *                 QJL mode the group's QJL sign word;
  *                 then (nu_t, gamma_t) float32 pairs for t = 0..page_tokens-1
- *                 (input norm, residual norm).
- *   value block = for coordinate pair i, for plane j in 0..value_bits-1: one
- *                 word whose bits 0..15 are plane j of slots 0..15 of
- *                 coordinate 2i and bits 16..31 the same for coordinate 2i+1;
- *                 then nu[page_tokens] float32.
+ *                 (input norm, then the residual norm or the scale s);
+ *                 then, with key_outliers = k > 0, per token a record
+ *                 [count u8][index u8 x k][pad to even][fp16 value x k][pad to 4].
+ *   value block = for coordinate pair i, for plane j in 0..b_i-1: one word
+ *                 whose bits 0..15 are plane j of slots 0..15 of coordinate 2i
+ *                 and bits 16..31 the same for coordinate 2i+1;
+ *                 then nu[page_tokens] float32 (LLOYD), or per token and
+ *                 32-coordinate group an (fp16 scale, fp16 zero) pair (GROUP).
  * A QJL bit is 1 where the projected residual is negative.  Bytes of slots at
  * or beyond a sequence's length are unspecified. */
 typedef struct {

@@ -20,13 +20,18 @@ TQ_OK = 0
 TQ_ROT_FWHT, TQ_ROT_DENSE = 0, 1
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 _ROT = {"fwht": TQ_ROT_FWHT, "dense": TQ_ROT_DENSE}
+_KEY_MODE = {"qjl": 0, "scaled_unbiased": 1, "scaled_mse": 2}
+_VALUE_MODE = {"lloyd": 0, "group": 1}
 _DTYPE = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
 
 
 class _Config(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("key_bits", ctypes.c_int32), ("value_bits", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("rotation", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("window", ctypes.c_int32), ("rotation", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("key_mode", ctypes.c_int32), ("value_mode", ctypes.c_int32), ("key_bits_hi", ctypes.c_int32),
+                ("value_bits_hi", ctypes.c_int32), ("key_outliers", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 class _Cache(ctypes.Structure):
@@ -113,10 +118,16 @@ class Config:
     window: int = 0
     rotation: str = "fwht"
     seed: int = 42
+    key_mode: str = "qjl"            # "qjl" | "scaled_unbiased" | "scaled_mse"
+    value_mode: str = "lloyd"        # "lloyd" | "group"
+    key_bits_hi: int = 0             # mixed-channel rate: bits of coordinates d/2.. (0 = key_bits)
+    value_bits_hi: int = 0
+    key_outliers: int = 0            # key sidecar entries per vector
 
     def c(self) -> _Config:
         return _Config(self.head_dim, self.num_q_heads, self.num_kv_heads, self.key_bits, self.value_bits,
-                       self.page_tokens, self.window, _ROT[self.rotation], self.seed)
+                       self.page_tokens, self.window, _ROT[self.rotation], self.seed, _KEY_MODE[self.key_mode],
+                       _VALUE_MODE[self.value_mode], self.key_bits_hi, self.value_bits_hi, self.key_outliers)
 
 
 TQ_STATUS_BAD_SLOT, TQ_STATUS_BAD_PAGE, TQ_STATUS_CAPACITY = 1, 2, 4

@@ -24,8 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq_hip.so")
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["tq_abi.cpp", "tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_dequant.hip",
-           "tq_scratch.hip"]
+SOURCES = ["tq_abi.cpp", "tq_host.cpp", "tq_append.hip", "tq_decode_mfma.hip", "tq_codec.hip", "tq_scratch.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -42,9 +42,23 @@ tq_status check_config(const tq_config* c) {
   if (c->num_q_heads / c->num_kv_heads > 8)
     return fail(TQ_ERR_UNSUPPORTED, "GQA group of %d query heads per kv head (max 8)",
                 c->num_q_heads / c->num_kv_heads);
-  if (c->key_bits < 2 || c->key_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "key_bits %d not in 2..4", c->key_bits);
+  if (c->key_mode != TQ_KEY_QJL && c->key_mode != TQ_KEY_SCALED_UNBIASED && c->key_mode != TQ_KEY_SCALED_MSE)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "key_mode %d unknown", c->key_mode);
+  if (c->value_mode != TQ_VALUE_LLOYD && c->value_mode != TQ_VALUE_GROUP)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "value_mode %d unknown", c->value_mode);
+  const int kmin = c->key_mode == TQ_KEY_QJL ? 2 : 1;
+  if (c->key_bits < kmin || c->key_bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "key_bits %d not in %d..4", c->key_bits, kmin);
+  if (c->key_bits_hi != 0 && (c->key_bits_hi < kmin || c->key_bits_hi > 4))
+    return fail(TQ_ERR_UNSUPPORTED, "key_bits_hi %d not 0 or in %d..4", c->key_bits_hi, kmin);
   if (c->value_bits < 1 || c->value_bits > 4)
     return fail(TQ_ERR_UNSUPPORTED, "value_bits %d not in 1..4", c->value_bits);
+  if (c->value_bits_hi < 0 || c->value_bits_hi > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "value_bits_hi %d not 0 or in 1..4", c->value_bits_hi);
+  if (c->key_outliers < 0 || c->key_outliers > tqi::kMaxOutliers)
+    return fail(TQ_ERR_UNSUPPORTED, "key_outliers %d not in 0..%d", c->key_outliers, tqi::kMaxOutliers);
+  if (c->reserved[0] || c->reserved[1] || c->reserved[2])
+    return fail(TQ_ERR_INVALID_ARGUMENT, "reserved config fields must be zero");
   if (c->page_tokens != 16) return fail(TQ_ERR_UNSUPPORTED, "page_tokens %d not supported (16)", c->page_tokens);
   if (c->window < 0 || c->window > 1024 || c->window % 16)
     return fail(TQ_ERR_UNSUPPORTED, "window %d must be 0 or a multiple of 16 up to 1024", c->window);
@@ -83,8 +97,9 @@ tqi::CacheView view(const tq_config* c, const tq_cache* k) {
   v.num_kv_heads = c->num_kv_heads;
   v.page_tokens = c->page_tokens;
   v.window = c->window;
-  v.key_block = int32_t(tqi::key_block_bytes(c->head_dim, c->key_bits, c->page_tokens));
-  v.value_block = int32_t(tqi::value_block_bytes(c->head_dim, c->value_bits, c->page_tokens));
+  v.codec = tqi::make_codec(*c);
+  v.key_block = v.codec.key_block;
+  v.value_block = v.codec.value_block;
   v.status = k->status;
   return v;
 }
@@ -100,12 +115,12 @@ size_t tq_params_bytes(const tq_config* cfg) {
 
 size_t tq_key_block_bytes(const tq_config* cfg) {
   if (check_config(cfg) != TQ_OK) return 0;
-  return tqi::key_block_bytes(cfg->head_dim, cfg->key_bits, cfg->page_tokens);
+  return tqi::key_block_bytes(*cfg);
 }
 
 size_t tq_value_block_bytes(const tq_config* cfg) {
   if (check_config(cfg) != TQ_OK) return 0;
-  return tqi::value_block_bytes(cfg->head_dim, cfg->value_bits, cfg->page_tokens);
+  return tqi::value_block_bytes(*cfg);
 }
 
 tq_status tq_init_codebooks(const tq_config* cfg, void* params_dev, void* params_host_or_null, void* stream) {
@@ -161,7 +176,8 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params_dev, const
   a.value_bits = cfg->value_bits;
   if ((long long)num_seqs * cfg->num_kv_heads * ((max_new_per_seq + 15) / 16 + 1) > 0x7fffffffLL)
     return fail(TQ_ERR_CAPACITY, "append launch too large");
-  const int e = tqi::launch_append(*cfg, a, num_seqs, max_new_per_seq, stream);
+  const int e = a.cache.codec.ext ? tqi::launch_append_codec(*cfg, a, num_seqs, max_new_per_seq, stream)
+                                  : tqi::launch_append(*cfg, a, num_seqs, max_new_per_seq, stream);
   if (e != 0) return hip_fail(e, "append launch");
   return TQ_OK;
 }
@@ -230,7 +246,7 @@ tq_status decode(const tq_config* cfg, const void* params_dev, const tq_cache* c
   a.max_ctx = mc;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
   const int e = tqi::decode_mfma_supported(*cfg) ? tqi::launch_decode_mfma(*cfg, a, stream)
-                                                 : tqi::launch_decode(*cfg, a, stream);
+                                                 : tqi::launch_decode_codec(*cfg, a, stream);
   if (e != 0) return hip_fail(e, "decode launch");
   return TQ_OK;
 }
@@ -278,7 +294,7 @@ tq_status tq_dequantize(const tq_config* cfg, const void* params_dev, const tq_c
   a.tok_end = tok_end;
   a.key_mse_bits = cfg->key_bits - 1;
   a.value_bits = cfg->value_bits;
-  const int e = tqi::launch_dequantize(*cfg, a, stream);
+  const int e = tqi::launch_dequantize_codec(*cfg, a, stream);
   if (e != 0) return hip_fail(e, "dequantize launch");
   return TQ_OK;
 }

@@ -1233,7 +1233,7 @@ size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads) {
 
 bool decode_mfma_supported(const tq_config& cfg) {
   return (cfg.head_dim == 128 || cfg.head_dim == 256) && cfg.num_q_heads / cfg.num_kv_heads <= kMaxG &&
-         cfg.page_tokens == kPage && cfg.window <= 1024;
+         cfg.page_tokens == kPage && cfg.window <= 1024 && !make_codec(cfg).ext;
 }
 
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream) {

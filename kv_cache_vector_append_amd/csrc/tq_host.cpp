@@ -226,7 +226,7 @@ void write_signs(uint8_t* blob, uint64_t seed, int d) {
 // a whole number of tiles (the matrix-core kernel's 128-token blocks, the
 // plain kernel's 64-token tiles).
 SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
-  const bool mfma = decode_mfma_supported(cfg);
+  const bool mfma = decode_mfma_supported(cfg);  // false for the extended formats
   const int units = (num_seqs > 0 ? num_seqs : 1) * cfg.num_kv_heads;
   const int tile = mfma ? 128 : 64;
   const int items = mfma ? decode_mfma_items(cfg) : 2048;
@@ -245,21 +245,56 @@ SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
   return {int(splits), int(split_tokens)};
 }
 
+Codec make_codec(const tq_config& c) {
+  Codec k{};
+  const int d = c.head_dim, P = c.page_tokens;
+  k.key_mode = c.key_mode;
+  k.value_mode = c.value_mode;
+  k.qjl = c.key_mode == TQ_KEY_QJL ? 1 : 0;
+  k.kbits[0] = c.key_bits - k.qjl;
+  k.kbits[1] = (c.key_bits_hi ? c.key_bits_hi : c.key_bits) - k.qjl;
+  k.vbits[0] = c.value_bits;
+  k.vbits[1] = c.value_bits_hi ? c.value_bits_hi : c.value_bits;
+  k.outliers = c.key_outliers;
+  k.ext = c.key_mode != TQ_KEY_QJL || c.value_mode != TQ_VALUE_LLOYD || k.kbits[0] != k.kbits[1] ||
+          k.vbits[0] != k.vbits[1] || c.key_outliers != 0;
+  const int half_groups = d / (2 * kGroup);
+  k.key_row_words = half_groups * (k.kbits[0] + k.qjl) + half_groups * (k.kbits[1] + k.qjl);
+  k.key_norm_off = 4 * P * k.key_row_words;
+  k.key_side_off = k.key_norm_off + 8 * P;
+  k.side_val_off = 1 + k.outliers + ((1 + k.outliers) & 1);
+  k.side_bytes = k.outliers ? (k.side_val_off + 2 * k.outliers + 3) / 4 * 4 : 0;
+  k.key_block = k.key_side_off + P * k.side_bytes;
+  k.value_words = (d / 4) * (k.vbits[0] + k.vbits[1]);
+  k.value_tail_off = 4 * k.value_words;
+  k.value_block = k.value_tail_off + (c.value_mode == TQ_VALUE_GROUP ? P * (d / kGroup) * 4 : 4 * P);
+  return k;
+}
+
 void build_params(const tq_config& cfg, uint8_t* blob) {
   const int d = cfg.head_dim;
+  const Codec k = make_codec(cfg);
   std::memset(blob, 0, params_bytes(d, cfg.rotation));
   ParamsHeader h{};
   h.magic = kParamsMagic;
-  h.version = 1;
+  h.version = 2;
   h.head_dim = d;
-  h.key_mse_bits = cfg.key_bits - 1;
-  h.value_bits = cfg.value_bits;
+  h.key_mse_bits = k.kbits[0];
+  h.value_bits = k.vbits[0];
   h.rotation = cfg.rotation;
   h.seed = cfg.seed;
   h.total_bytes = uint32_t(params_bytes(d, cfg.rotation));
+  h.key_mse_bits_hi = k.kbits[1];
+  h.value_bits_hi = k.vbits[1];
+  h.key_mode = cfg.key_mode;
+  h.value_mode = cfg.value_mode;
+  h.key_outliers = cfg.key_outliers;
   std::memcpy(blob, &h, sizeof(h));
-  write_codebook(blob, kOffKeyCentroids, kOffKeyThresholds, kOffKeyPlaneCoef, d, cfg.key_bits - 1);
-  write_codebook(blob, kOffValueCentroids, kOffValueThresholds, kOffValuePlaneCoef, d, cfg.value_bits);
+  for (int half = 0; half < 2; ++half) {
+    const int o = half ? kOffUpperHalf : 0;
+    write_codebook(blob, kOffKeyCentroids + o, kOffKeyThresholds + o, kOffKeyPlaneCoef + o, d, k.kbits[half]);
+    write_codebook(blob, kOffValueCentroids + o, kOffValueThresholds + o, kOffValuePlaneCoef + o, d, k.vbits[half]);
+  }
   write_signs(blob, cfg.seed, d);
   if (cfg.rotation == TQ_ROT_DENSE) {
     float* dst = reinterpret_cast<float*>(blob + kOffDense);

@@ -18,6 +18,9 @@ namespace tqi {
 //   [256, 320)     value thresholds, float[16]
 //   [320, 384)     key bit-plane coefficients, float[16] (see below)
 //   [384, 448)     value bit-plane coefficients, float[16]
+//   [448, 832)     the same six tables for the upper coordinate half d/2 .. d-1
+//                  (key_bits_hi / value_bits_hi; copies of the lower ones
+//                  when the rate is uniform)
 //   [1024, 1280)   Rademacher sign words, 4 roles x 64 bytes (coordinate i of a
 //                  role is bit i % 32 of uint32 word i / 32; 1 means -1)
 //   [2048, ...)    dense variant: Pi_K, G, Pi_V as float[d*d] row-major each,
@@ -39,6 +42,7 @@ constexpr int kOffValueCentroids = 192;
 constexpr int kOffValueThresholds = 256;
 constexpr int kOffKeyPlaneCoef = 320;
 constexpr int kOffValuePlaneCoef = 384;
+constexpr int kOffUpperHalf = 384;  // add to a lower-half table offset for its upper-half copy
 constexpr int kOffSigns = 1024;
 constexpr int kSignRoleBytes = 64;
 constexpr int kOffDense = 2048;
@@ -54,7 +58,8 @@ struct ParamsHeader {
   int32_t rotation;
   uint64_t seed;
   uint32_t total_bytes;
-  uint32_t reserved[7];
+  int32_t key_mse_bits_hi, value_bits_hi, key_mode, value_mode, key_outliers;
+  uint32_t reserved[2];
 };
 static_assert(sizeof(ParamsHeader) == 64, "header is 64 bytes");
 
@@ -64,8 +69,32 @@ inline size_t params_bytes(int d, int rotation) {
 // byte offset of the fp16 split of dense matrix m (0 Pi_K, 1 G, 2 Pi_V); lo follows hi
 constexpr size_t dense16_offset(int d, int m) { return kOffDense + size_t(3) * d * d * 4 + size_t(m) * d * d * 4; }
 constexpr float kDense16Scale[3] = {1024.f, 256.f, 1024.f};
-inline size_t key_block_bytes(int d, int key_bits, int P) { return size_t(key_bits) * P * d / 8 + 8 * size_t(P); }
-inline size_t value_block_bytes(int d, int value_bits, int P) { return size_t(value_bits) * P * d / 8 + 4 * size_t(P); }
+
+// ---------------------------------------------------------------------------
+// Stored format of one configuration (built on the host from tq_config).
+// Coordinates d/2 .. d-1 form the upper half, with their own bit counts.
+// ---------------------------------------------------------------------------
+constexpr int kGroup = 32;         // coordinates per key word and per value scale/zero group
+constexpr int kMaxOutliers = 8;
+struct Codec {
+  int32_t ext;                     // any feature beyond the default format
+  int32_t key_mode, value_mode;    // tq_key_mode, tq_value_mode
+  int32_t kbits[2];                // key Lloyd-Max bits of the lower / upper half
+  int32_t vbits[2];                // value bits of the lower / upper half
+  int32_t qjl;                     // 1: a QJL plane per key group
+  int32_t outliers;                // key sidecar entries per vector
+  int32_t key_row_words;           // code words per token in a key block
+  int32_t key_norm_off;            // bytes: (nu, gamma or s) pairs
+  int32_t key_side_off;            // bytes: sidecar records
+  int32_t side_bytes;              // bytes per sidecar record
+  int32_t side_val_off;            // bytes: fp16 values inside a record
+  int32_t value_words;             // code words in a value block
+  int32_t value_tail_off;          // bytes: nu[] or the (scale, zero) pairs
+  int32_t key_block, value_block;  // bytes
+};
+Codec make_codec(const tq_config& cfg);
+inline size_t key_block_bytes(const tq_config& cfg) { return size_t(make_codec(cfg).key_block); }
+inline size_t value_block_bytes(const tq_config& cfg) { return size_t(make_codec(cfg).value_block); }
 
 // ---------------------------------------------------------------------------
 // Launch argument blocks.
@@ -80,6 +109,7 @@ struct CacheView {
   int32_t num_kv_heads, page_tokens, window;
   int32_t key_block, value_block;  // bytes
   uint32_t* status;                // optional TQ_STATUS_* word
+  Codec codec;
 };
 
 struct AppendArgs {
@@ -131,12 +161,15 @@ void build_params(const tq_config& cfg, uint8_t* blob);
 
 // Kernel launchers (one per .hip file); return hipError_t as int.
 int launch_append(const tq_config& cfg, const AppendArgs& a, int num_seqs, int max_new, void* stream);
-int launch_decode(const tq_config& cfg, const DecodeArgs& a, void* stream);
+// the generic path (tq_codec.hip): every stored format, one wavefront per page
+// of append, a per-lane scoring decode, and the reconstruction
+int launch_append_codec(const tq_config& cfg, const AppendArgs& a, int num_seqs, int max_new, void* stream);
+int launch_decode_codec(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
 int decode_mfma_items(const tq_config& cfg);  // (sequence, KV head, split) work items that fill the GPU once
 size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-operand region at the workspace start
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
-int launch_dequantize(const tq_config& cfg, const DequantArgs& a, void* stream);
+int launch_dequantize_codec(const tq_config& cfg, const DequantArgs& a, void* stream);
 
 // Device address of the current GPU's library-owned decode workspace of
 // TQ_STATIC_WORKSPACE_BYTES (tq_scratch.hip); returns hipError_t as int.

@@ -30,14 +30,24 @@ def lib():
     return tqa
 
 
-def oracle_config(w: workloads.Workload) -> tq.Config:
-    return tq.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
-                     w.window, w.rotation, w.method_seed)
+FORMAT_FIELDS = ("key_mode", "value_mode", "key_bits_hi", "value_bits_hi", "key_outliers")
+
+
+def _format(w):
+    return {f: getattr(w, f) for f in FORMAT_FIELDS}
+
+
+def oracle_config(w: workloads.Workload, **over) -> tq.Config:
+    kw = dict(head_dim=w.head_dim, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, key_bits=w.key_bits,
+              value_bits=w.value_bits, page_tokens=w.page_tokens, window=w.window, rotation=w.rotation,
+              seed=w.method_seed, **_format(w))
+    kw.update(over)
+    return tq.Config(**kw)
 
 
 def lib_config(w: workloads.Workload):
     return lib().Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
-                        w.window, w.rotation, w.method_seed)
+                        w.window, w.rotation, w.method_seed, **_format(w))
 
 
 @dataclass
@@ -120,10 +130,33 @@ def _near_threshold(y, t):
     return np.min(np.abs(y[..., None] - np.asarray(t)[None, :]), axis=-1) < BAND if len(t) else np.zeros(y.shape, bool)
 
 
+def near_threshold(y, t_lo, t_hi):
+    """|y - t| < BAND for the thresholds of each coordinate's half."""
+    d = y.shape[-1]
+    return np.concatenate([_near_threshold(y[..., :d // 2], t_lo), _near_threshold(y[..., d // 2:], t_hi)], axis=-1)
+
+
+def key_aux(P, y, codes, nu):
+    """The second fp32 of a key and, in the QJL mode, the projected residual w,
+    recomputed in float64 from the given codes: (aux, w)."""
+    yhat = tq.key_centroids(P, codes)
+    zero = nu == 0
+    if P.cfg.qjl:
+        e = y - yhat
+        return np.where(zero, 0.0, np.linalg.norm(e, axis=-1)), P.T.sketch(e)
+    ip = (y * yhat).sum(-1)
+    if P.cfg.key_mode == "scaled_unbiased":
+        s = nu / np.where(zero, 1.0, ip)
+    else:
+        s = nu * ip / np.where(zero, 1.0, (yhat * yhat).sum(-1))
+    return np.where(zero, 0.0, s), None
+
+
 def compare_append(run: Run, gc: tq.Cache | None = None, positions=None) -> AppendReport:
     """Compare GPU pages with the oracle's encoding of the same inputs."""
     gc = gc if gc is not None else gpu_cache_as_oracle(run)
     P, d, H = run.P, run.ocfg.head_dim, run.ocfg.num_kv_heads
+    cfg = run.ocfg
     rep = AppendReport()
     for s, n in enumerate(run.lens):
         pos = np.arange(n) if positions is None else np.asarray(positions[s])
@@ -137,37 +170,56 @@ def compare_append(run: Run, gc: tq.Cache | None = None, positions=None) -> Appe
         rep.tokens += len(pos) * H
         gk = g["k_codes"].reshape(-1, d).astype(np.int64)
         gz = g["k_z"].reshape(-1, d)
+        # sidecar: bit-exact (its selection and fp16 values involve no rotation)
+        if cfg.key_outliers:
+            kk = cfg.key_outliers
+            gcnt = g["k_side_cnt"].reshape(-1)
+            rep.unexcused += int((gcnt != ek["side_count"]).sum())
+            used = np.arange(kk)[None, :] < ek["side_count"][:, None]
+            gi = g["k_side_idx"].reshape(-1, kk)
+            gv = g["k_side_val"].reshape(-1, kk).view(np.uint16)
+            rep.unexcused += int(((gi != ek["side_idx"]) & used).sum())
+            rep.unexcused += int(((gv != ek["side_val"].view(np.uint16)) & used).sum())
         # key codes
         mism = gk != ek["codes"]
-        near = _near_threshold(ek["y"], P.kt)
+        near = near_threshold(ek["y"], P.kt, P.kt_hi)
         rep.unexcused += int((mism & ~near).sum())
         rep.key_code_flips += int((mism & near).sum())
         flipped_tok = mism.any(axis=1)
-        # QJL bits: re-derive from the GPU's codes where a code flipped
-        e = ek["y"] - P.kc[gk]
-        w = np.where(flipped_tok[:, None], P.T.sketch(e), ek["w"])
-        zexp = w < 0
-        zero = ek["nu"] == 0
-        zexp[zero] = False
-        zm = gz != zexp
-        zband = np.abs(w) / np.sqrt(d) < BAND
-        rep.unexcused += int((zm & ~zband).sum())
-        rep.qjl_band_flips += int((zm & zband).sum())
-        # norms
-        gnu = g["k_nu"].reshape(-1).astype(np.float64)
-        ggam = g["k_gamma"].reshape(-1).astype(np.float64)
+        # the second fp32 and the QJL bits, re-derived from the GPU's codes where a code flipped
         onu = ek["nu"]
-        ogam = np.where(zero, 0.0, np.linalg.norm(e, axis=1))
+        zero = onu == 0
+        oaux, w = key_aux(P, ek["y"], gk, onu)
+        if cfg.qjl:
+            zexp = w < 0
+            zexp[zero] = False
+            zm = gz != zexp
+            zband = np.abs(w) / np.sqrt(d) < BAND
+            rep.unexcused += int((zm & ~zband).sum())
+            rep.qjl_band_flips += int((zm & zband).sum())
+        else:
+            rep.unexcused += int(gz.sum())                           # no QJL plane is stored
+        gnu = g["k_nu"].reshape(-1).astype(np.float64)
+        gaux = g["k_gamma"].reshape(-1).astype(np.float64)
         rep.max_nu_rel = max(rep.max_nu_rel, float(np.max(np.abs(gnu - onu) / np.maximum(onu, 1e-30))))
-        rep.max_gamma_rel = max(rep.max_gamma_rel, float(np.max(np.abs(ggam - ogam) / np.maximum(ogam, 1e-30))))
+        rep.max_gamma_rel = max(rep.max_gamma_rel,
+                                float(np.max(np.abs(gaux - oaux) / np.maximum(np.abs(oaux), 1e-30))))
         # value codes
         gv = g["v_codes"].reshape(-1, d).astype(np.int64)
-        vm = gv != ev["codes"]
-        vnear = _near_threshold(ev["y"], P.vt)
-        rep.unexcused += int((vm & ~vnear).sum())
-        rep.value_code_flips += int((vm & vnear).sum())
-        gvn = g["v_nu"].reshape(-1).astype(np.float64)
-        rep.max_nu_rel = max(rep.max_nu_rel, float(np.max(np.abs(gvn - ev["nu"]) / np.maximum(ev["nu"], 1e-30))))
+        if cfg.value_mode == "group":
+            # decided in float32 on both sides: bit-exact codes, scales and zeros
+            rep.unexcused += int((gv != ev["codes"]).sum())
+            rep.unexcused += int((g["v_scale"].reshape(ev["scale"].shape).view(np.uint16)
+                                  != ev["scale"].view(np.uint16)).sum())
+            rep.unexcused += int((g["v_zero"].reshape(ev["zero"].shape).view(np.uint16)
+                                  != ev["zero"].view(np.uint16)).sum())
+        else:
+            vm = gv != ev["codes"]
+            vnear = near_threshold(ev["y"], P.vt, P.vt_hi)
+            rep.unexcused += int((vm & ~vnear).sum())
+            rep.value_code_flips += int((vm & vnear).sum())
+            gvn = g["v_nu"].reshape(-1).astype(np.float64)
+            rep.max_nu_rel = max(rep.max_nu_rel, float(np.max(np.abs(gvn - ev["nu"]) / np.maximum(ev["nu"], 1e-30))))
         # fp16 window
         W = run.ocfg.window
         if W and positions is None:
@@ -186,7 +238,8 @@ def aligned_oracle_cache(run: Run, gc: tq.Cache | None = None):
     """The oracle's own cache, except that where the GPU took the other side of a
     near-threshold decision, the oracle adopts the GPU's decision:
       * a code with |y - t| < 1e-6: the oracle takes the GPU's codes and
-        recomputes that token's residual norm and QJL bits itself in float64;
+        recomputes that token's second fp32 (residual norm or scale) and QJL
+        bits itself in float64;
       * a QJL bit with |w_j| / sqrt(d) < 1e-6 (the sign decision's threshold
         is 0): the oracle takes the GPU's bit.
 
@@ -210,35 +263,37 @@ def aligned_oracle_cache(run: Run, gc: tq.Cache | None = None):
         o = oc.gather(s, pos)
         km = (g["k_codes"] != o["k_codes"]).any(axis=-1)          # [n, H]
         for (i, h) in np.argwhere(km):
-            x = run.K[s][i, h].double().numpy()[None]
-            ek = tq.encode_keys(P, x)
+            ek = tq.encode_keys(P, run.K[s][i, h].double().numpy()[None])
             codes = g["k_codes"][i, h].astype(np.int64)
-            near = np.min(np.abs(ek["y"][0][:, None] - P.kt[None, :]), axis=-1) < BAND
+            near = near_threshold(ek["y"], P.kt, P.kt_hi)[0]
             if not np.all((codes == ek["codes"][0]) | near):
                 continue                                           # a real mismatch stays visible
-            e = ek["y"][0] - P.kc[codes]
-            w = P.T.sketch(e[None])[0]
+            aux, w = key_aux(P, ek["y"], codes[None], ek["nu"])
             oc.k_codes[pg[i], h, t[i]] = codes
-            oc.k_z[pg[i], h, t[i]] = w < 0
-            oc.k_gamma[pg[i], h, t[i]] = np.float32(np.linalg.norm(e))
+            if w is not None:
+                oc.k_z[pg[i], h, t[i]] = (w[0] < 0) & (ek["nu"][0] > 0)
+            oc.k_gamma[pg[i], h, t[i]] = np.float32(aux[0])
             adjusted += 1
-        # QJL bits on the (now aligned) codes: adopt in-band sign decisions
-        o = oc.gather(s, pos)
-        zm = (g["k_z"] != o["k_z"]).any(axis=-1)
-        for (i, h) in np.argwhere(zm):
-            ek = tq.encode_keys(P, run.K[s][i, h].double().numpy()[None])
-            e = ek["y"][0] - P.kc[o["k_codes"][i, h].astype(np.int64)]
-            w = P.T.sketch(e[None])[0]
-            diff = g["k_z"][i, h] != o["k_z"][i, h]
-            if ek["nu"][0] == 0 or not np.all(np.abs(w[diff]) / np.sqrt(d) < BAND):
-                continue                                           # a real mismatch stays visible
-            oc.k_z[pg[i], h, t[i]] = g["k_z"][i, h]
-            adjusted += 1
+        if run.ocfg.qjl:
+            # QJL bits on the (now aligned) codes: adopt in-band sign decisions
+            o = oc.gather(s, pos)
+            zm = (g["k_z"] != o["k_z"]).any(axis=-1)
+            for (i, h) in np.argwhere(zm):
+                ek = tq.encode_keys(P, run.K[s][i, h].double().numpy()[None])
+                e = ek["y"][0] - tq.key_centroids(P, o["k_codes"][i, h][None])[0]
+                w = P.T.sketch(e[None])[0]
+                diff = g["k_z"][i, h] != o["k_z"][i, h]
+                if ek["nu"][0] == 0 or not np.all(np.abs(w[diff]) / np.sqrt(d) < BAND):
+                    continue                                       # a real mismatch stays visible
+                oc.k_z[pg[i], h, t[i]] = g["k_z"][i, h]
+                adjusted += 1
+        if run.ocfg.value_mode == "group":
+            continue                                               # decided in float32 on both sides: no band
         vm = (g["v_codes"] != o["v_codes"]).any(axis=-1)
         for (i, h) in np.argwhere(vm):
             ev = tq.encode_values(P, run.V[s][i, h].double().numpy()[None])
             codes = g["v_codes"][i, h].astype(np.int64)
-            near = np.min(np.abs(ev["y"][0][:, None] - P.vt[None, :]), axis=-1) < BAND
+            near = near_threshold(ev["y"], P.vt, P.vt_hi)[0]
             if not np.all((codes == ev["codes"][0]) | near):
                 continue
             oc.v_codes[pg[i], h, t[i]] = codes

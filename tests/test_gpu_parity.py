@@ -13,7 +13,7 @@ import workloads
 from oracle import tq
 
 from harness import (DECODE_TOL, NORM_RTOL, aligned_oracle_cache, compare_append, decode_error,
-                     gpu_cache_as_oracle, gpu_decode, make_run, queries)
+                     gpu_cache_as_oracle, gpu_decode, make_run, oracle_config, queries)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,15 @@ CASES = {
     "dense_short_appends": ("dense_short_appends", [40, 13], 8),
     # dense rotation at head_dim 64 (the wavefront-per-token kernel)
     "dense_hd64": ("dense_hd64", [100, 37], 3),
+    # extended formats, on the generic path
+    "mixed_3p5_2p5": ("mixed_3p5_2p5", [700, 129, 300], 2),
+    "mixed_dense_hd256": ("mixed_dense_hd256", [300, 77], 1),
+    "scaled_unbiased_3p5_3": ("scaled_unbiased_3p5_3", [520, 33, 257], 2),
+    "scaled_mse_dense_hd256": ("scaled_mse_dense_hd256", [300, 77], 1),
+    "outlier_sidecar": ("outlier_sidecar", [520, 260, 1], 1),
+    "group_values": ("group_values", [400, 3, 160, 0], 3),
+    "group_values_dense_hd256": ("group_values_dense_hd256", [300, 77], 1),
+    "every_feature_hd64_gqa8": ("every_feature_hd64_gqa8", [300, 130], 2),
 }
 
 import workloads as _w
@@ -57,6 +66,19 @@ _w.WORKLOADS.setdefault("dense_short_appends", _w.HD256_DENSE_32.replace(name="d
 _w.WORKLOADS.setdefault("plain_hd128_gqa8", _w.GQA_DECODE.replace(
     name="plain_hd128_gqa8", num_q_heads=16, num_kv_heads=2, key_bits=4, value_bits=2, window=48,
     rotation="dense"))
+for _name in ("mixed_3p5_2p5", "scaled_unbiased_3p5_3", "outlier_sidecar", "group_values"):
+    _w.WORKLOADS.setdefault(_name, _w.WORKLOADS[_name + "_decode"].replace(
+        name=_name, num_q_heads=8, num_kv_heads=2))
+_w.WORKLOADS.setdefault("mixed_dense_hd256", _w.HD256_DENSE_32.replace(
+    name="mixed_dense_hd256", key_bits=3, key_bits_hi=4, value_bits=2, value_bits_hi=4))
+_w.WORKLOADS.setdefault("scaled_mse_dense_hd256", _w.HD256_DENSE_32.replace(
+    name="scaled_mse_dense_hd256", key_mode="scaled_mse", key_bits=2, value_bits=2))
+_w.WORKLOADS.setdefault("group_values_dense_hd256", _w.HD256_DENSE_44.replace(
+    name="group_values_dense_hd256", value_mode="group"))
+_w.WORKLOADS.setdefault("every_feature_hd64_gqa8", _w.GQA_DECODE.replace(
+    name="every_feature_hd64_gqa8", num_q_heads=16, num_kv_heads=2, head_dim=64, key_mode="scaled_unbiased",
+    key_bits=2, key_bits_hi=3, value_mode="group", value_bits=2, value_bits_hi=3, key_outliers=3, window=32,
+    k_dist="normal_outlier"))
 
 _RUNS = {}
 _PARAMS = {}
@@ -67,7 +89,7 @@ def _run(name):
         wname, lens, chunks = CASES[name]
         w = workloads.WORKLOADS[wname]
         print(f"[parity] append {name} lens={lens} chunks={chunks}", flush=True)
-        key = (w.head_dim, w.key_bits, w.value_bits, w.rotation)
+        key = oracle_config(w)
         run = make_run(w, lens, chunks=chunks, P=_PARAMS.get(key))
         _PARAMS[key] = run.P
         _RUNS[name] = run
@@ -109,7 +131,9 @@ def test_decode_parity(name):
             assert np.all(o_gpu[s] == 0)
 
 
-@pytest.mark.parametrize("name", ["gqa_decode", "hd256_long_dense_4_4", "outlier_stress"])
+@pytest.mark.parametrize("name", ["gqa_decode", "hd256_long_dense_4_4", "outlier_stress", "mixed_dense_hd256",
+                                  "scaled_unbiased_3p5_3", "outlier_sidecar", "group_values",
+                                  "every_feature_hd64_gqa8"])
 def test_dequantize_parity(name):
     import kv_cache_vector_append_amd as tqa
     run = _run(name)
@@ -128,10 +152,11 @@ def test_dequantize_parity(name):
             assert err < 1e-5, err
 
 
-def test_decode_matches_attention_over_gpu_dequantized():
+@pytest.mark.parametrize("name", ["gqa_decode", "scaled_unbiased_3p5_3", "outlier_sidecar"])
+def test_decode_matches_attention_over_gpu_dequantized(name):
     # invariant: compressed-domain decode == exact attention over the dequantized cache
     import kv_cache_vector_append_amd as tqa
-    run = _run("gqa_decode")
+    run = _run(name)
     H, d, G = run.w.num_kv_heads, run.w.head_dim, run.w.gqa
     q = queries(run.w, len(run.lens))
     o_gpu, _ = gpu_decode(run, q)
@@ -153,7 +178,7 @@ def test_decode_matches_attention_over_gpu_dequantized():
 
 def test_append_is_deterministic():
     w = workloads.GQA_DECODE
-    a = make_run(w, [333, 50], oracle_append=False, P=_PARAMS.get((128, 3, 2, "fwht")))
+    a = make_run(w, [333, 50], oracle_append=False)
     b = make_run(w, [333, 50], oracle_append=False, P=a.P)
     for s, n in enumerate([333, 50]):
         ga, gb = gpu_cache_as_oracle(a).gather(s, np.arange(n)), gpu_cache_as_oracle(b).gather(s, np.arange(n))

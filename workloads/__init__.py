@@ -48,6 +48,13 @@ class Workload:
     method_seed: int = 42
     outlier_channels: int = 4
     outlier_scale: float = 20.0
+    # stored format beyond the default (mixed-channel rates, scaled keys, key
+    # outlier sidecar, group-quantized values); see the library's tq_config
+    key_mode: str = "qjl"
+    value_mode: str = "lloyd"
+    key_bits_hi: int = 0
+    value_bits_hi: int = 0
+    key_outliers: int = 0
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -237,3 +244,37 @@ def device_kv(w: Workload, which: str, num_tokens: int, g: torch.Generator, devi
 def device_queries(w: Workload, num_seqs: int, g: torch.Generator, device) -> torch.Tensor:
     x = torch.randn((num_seqs, w.num_q_heads, w.head_dim), generator=g, dtype=torch.float64, device=device)
     return x.to(w.torch_dtype).contiguous()
+
+
+# Extended stored formats ([Design Study] "Packed format and complete bit
+# accounting", "Final recommendation and expected gains"; [Reconstruction]
+# "The DRIVE/EDEN Mathematical Critique", "12. TurboVec Additions and
+# Divergences", section 11; [README] "How It Works" item 4), on the decode
+# shape of the mixed serving step (256 sequences x 4096 tokens, 32 q / 8 KV
+# heads, d = 128, bf16 N(0,1)) unless stated.
+_EXT_BASE = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_tokens=16, window=128, rotation="fwht",
+                 input_dtype="bf16", decode_seqs=256, decode_ctx=4096, input_seed=1006)
+
+MIXED_DECODE = _register(Workload(
+    name="mixed_3p5_2p5_decode",
+    description="256 x 4096 ctx, 32 q / 8 KV heads, d=128, bf16 N(0,1); mixed-channel rates: keys 3.5 bpc "
+                "(64 channels at 2+1 bits, 64 at 3+1), values 2.5 bpc (64 at 2, 64 at 3); FWHT",
+    key_bits=3, key_bits_hi=4, value_bits=2, value_bits_hi=3, **_EXT_BASE))
+
+SCALED_DECODE = _register(Workload(
+    name="scaled_unbiased_3p5_3_decode",
+    description="256 x 4096 ctx, 32 q / 8 KV heads, d=128, bf16 N(0,1); the recommended first product mode: "
+                "keys 3.5 bpc all Lloyd-Max with the length-renormalized scale, values 3.0 bpc; FWHT",
+    key_mode="scaled_unbiased", key_bits=3, key_bits_hi=4, value_bits=3, **_EXT_BASE))
+
+GROUP_DECODE = _register(Workload(
+    name="group_values_decode",
+    description="256 x 4096 ctx, 32 q / 8 KV heads, d=128, bf16 N(0,1); 3-bit QJL keys, 2-bit group-quantized "
+                "values (fp16 scale and zero per 32 coordinates, no rotation); FWHT",
+    key_bits=3, value_bits=2, value_mode="group", **_EXT_BASE))
+
+SIDECAR_DECODE = _register(OUTLIER_STRESS.replace(
+    name="outlier_sidecar_decode",
+    description="the outlier-stress workload (batch 4, 131072 ctx, 4 fixed channels per head x20, V Student-t(3), "
+                "4/4-bit, FWHT) with a 4-entry key outlier sidecar",
+    key_outliers=4))
