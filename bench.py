@@ -43,9 +43,17 @@ def log(msg):
 
 
 def record_bytes(w):
+    """Stored bytes per token-head: key = code bits (+ d/8 QJL signs) + the two
+    fp32 of the key (+ the sidecar record); value = code bits + nu (or the fp16
+    scale/zero pairs of group-quantized values)."""
     d = w.head_dim
-    key = w.key_bits * d // 8 + 8          # (b-1) d/8 codes + d/8 QJL signs + nu + gamma
-    value = w.value_bits * d // 8 + 4      # b d/8 codes + nu
+    kb = (w.key_bits + (w.key_bits_hi or w.key_bits)) * d // 16        # each half at its own rate
+    key = kb + 8
+    if w.key_outliers:
+        head = 1 + w.key_outliers + ((1 + w.key_outliers) & 1)
+        key += (head + 2 * w.key_outliers + 3) // 4 * 4
+    value = (w.value_bits + (w.value_bits_hi or w.value_bits)) * d // 16
+    value += d // 32 * 4 if w.value_mode == "group" else 4
     return key, value
 
 
@@ -205,6 +213,13 @@ class Setup:
     pass
 
 
+def library_config(w, tqa):
+    """The library's tq_config of a workload, stored format included."""
+    return tqa.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
+                      w.window, w.rotation, w.method_seed, key_mode=w.key_mode, value_mode=w.value_mode,
+                      key_bits_hi=w.key_bits_hi, value_bits_hi=w.value_bits_hi, key_outliers=w.key_outliers)
+
+
 def build_decode_setup(w, tqa, torch, dev, keep_head=None):
     """Cache filled with decode_ctx - 1 tokens per sequence; the step appends token
     decode_ctx - 1 of every sequence and decodes over decode_ctx tokens.
@@ -214,8 +229,7 @@ def build_decode_setup(w, tqa, torch, dev, keep_head=None):
     S = Setup()
     nseq, ctx = w.decode_seqs, w.decode_ctx
     mpp = w.pages_per_seq(ctx)
-    S.cfg = tqa.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
-                       w.window, w.rotation, w.method_seed)
+    S.cfg = library_config(w, tqa)
     S.params = torch.empty(tqa.params_bytes(S.cfg), dtype=torch.uint8, device=dev)
     tqa.init_codebooks(S.cfg, S.params)
     bt = workloads.block_table(w, nseq, mpp)
@@ -263,8 +277,7 @@ def build_mixed_setup(w, tqa, torch, dev):
     S = Setup()
     nseq, ctx, npre, ntok = w.decode_seqs, w.decode_ctx, w.prefill_seqs, w.prefill_tokens
     mpp = w.pages_per_seq(ctx)
-    S.cfg = tqa.Config(w.head_dim, w.num_q_heads, w.num_kv_heads, w.key_bits, w.value_bits, w.page_tokens,
-                       w.window, w.rotation, w.method_seed)
+    S.cfg = library_config(w, tqa)
     S.params = torch.empty(tqa.params_bytes(S.cfg), dtype=torch.uint8, device=dev)
     tqa.init_codebooks(S.cfg, S.params)
     bt = workloads.block_table(w, nseq, mpp)
@@ -499,9 +512,14 @@ def cpu_baseline(w, reps=4):
 # widths, the dense rotation's matrix-core append, and the latency-bound GQA
 # decode.
 EXTRA_WORKLOADS = ("mixed_serving", "hd256_long_dense_3_2", "hd256_long_dense_4_4", "hd256_dense_prefill",
-                   "gqa_decode")
-# (sequence, kv head) whose query group the quality metrics cover
-QUALITY_HEAD = {"outlier_stress": (2, 5)}
+                   "gqa_decode",
+                   # extended stored formats (the generic path): mixed-channel rates, scaled keys,
+                   # group-quantized values, and the outlier workload with a key sidecar
+                   "mixed_3p5_2p5_decode", "scaled_unbiased_3p5_3_decode", "group_values_decode",
+                   "outlier_sidecar_decode")
+# (sequence, kv head) whose query group the quality metrics cover (the same
+# head with and without the key sidecar)
+QUALITY_HEAD = {"outlier_stress": (2, 5), "outlier_sidecar_decode": (2, 5)}
 # what the decode arithmetic is: scores and value sums on the matrix cores with
 # the fp32 query / softmax weights carried as four fp8 parts against fp4 code
 # bit-planes, accumulated in fp32
@@ -596,8 +614,14 @@ def main(argv=None):
                 continue
             torch.cuda.empty_cache()
             ew = workloads.WORKLOADS[name]
-            er = run_gpu(ew, 10, 3, 0)
+            er = run_gpu(ew, 10, 3, 0, keep_head=QUALITY_HEAD.get(name))
             extra[name] = step_summary(ew, er, 10)
+            extra[name]["format"] = {"key_mode": ew.key_mode, "key_bits": [ew.key_bits, ew.key_bits_hi or ew.key_bits],
+                                     "value_mode": ew.value_mode,
+                                     "value_bits": [ew.value_bits, ew.value_bits_hi or ew.value_bits],
+                                     "key_outliers": ew.key_outliers, "rotation": ew.rotation}
+            if name in QUALITY_HEAD:
+                extra[name]["quality_vs_exact"] = quality_vs_exact(ew, er["setup"])
             del er
         line["other_workloads"] = extra
     if baseline is not None:

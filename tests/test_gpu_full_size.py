@@ -29,7 +29,7 @@ import torch
 
 import bench
 import workloads
-from harness import BAND, DECODE_TOL, NORM_RTOL, _near_threshold, decode_error
+from harness import BAND, DECODE_TOL, NORM_RTOL, decode_error, key_aux, near_threshold, oracle_config
 from oracle import tq
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +38,7 @@ DEV = torch.device("cuda:0")
 
 
 def _ocfg(w, num_q_heads=None, num_kv_heads=None):
-    return tq.Config(w.head_dim, num_q_heads or w.num_q_heads, num_kv_heads or w.num_kv_heads, w.key_bits,
-                     w.value_bits, w.page_tokens, w.window, w.rotation, w.method_seed)
+    return oracle_config(w, num_q_heads=num_q_heads or w.num_q_heads, num_kv_heads=num_kv_heads or w.num_kv_heads)
 
 
 def _sample_positions(w, L, rng, extra=24):
@@ -78,26 +77,38 @@ def _check_append(w, P, cache, bt, samples, inputs):
         gk = c.k_codes[pg, :, t].reshape(-1, d).astype(np.int64)
         gz = c.k_z[pg, :, t].reshape(-1, d)
         mism = gk != ek["codes"]
-        near = _near_threshold(ek["y"], P.kt)
+        near = near_threshold(ek["y"], P.kt, P.kt_hi)
         assert not (mism & ~near).any(), f"slot {slot}: key codes differ away from a threshold"
         flips += int(mism.sum())
-        e = ek["y"] - P.kc[gk]
-        wv = np.where(mism.any(axis=1)[:, None], P.T.sketch(e), ek["w"])
-        zexp = wv < 0
-        zexp[ek["nu"] == 0] = False
-        zm = gz != zexp
-        assert not (zm & ~(np.abs(wv) / np.sqrt(d) < BAND)).any(), f"slot {slot}: QJL bits differ"
+        oaux, wv = key_aux(P, ek["y"], gk, ek["nu"])
+        if cfg.qjl:
+            zexp = wv < 0
+            zexp[ek["nu"] == 0] = False
+            zm = gz != zexp
+            assert not (zm & ~(np.abs(wv) / np.sqrt(d) < BAND)).any(), f"slot {slot}: QJL bits differ"
+        if cfg.key_outliers:
+            assert np.array_equal(c.k_side_cnt[pg, :, t].reshape(-1), ek["side_count"])
+            used = np.arange(cfg.key_outliers)[None, :] < ek["side_count"][:, None]
+            gi = c.k_side_idx[pg, :, t].reshape(-1, cfg.key_outliers)
+            gsv = c.k_side_val[pg, :, t].reshape(-1, cfg.key_outliers).view(np.uint16)
+            assert not ((gi != ek["side_idx"]) & used).any() and not ((gsv != ek["side_val"].view(np.uint16)) & used).any()
         gnu = c.k_nu[pg, :, t].reshape(-1).astype(np.float64)
-        ggam = c.k_gamma[pg, :, t].reshape(-1).astype(np.float64)
-        ogam = np.where(ek["nu"] == 0, 0.0, np.linalg.norm(e, axis=1))
+        gaux = c.k_gamma[pg, :, t].reshape(-1).astype(np.float64)
         assert np.all(np.abs(gnu - ek["nu"]) <= NORM_RTOL * np.maximum(ek["nu"], 1e-30))
-        assert np.all(np.abs(ggam - ogam) <= NORM_RTOL * np.maximum(ogam, 1e-30))
+        assert np.all(np.abs(gaux - oaux) <= NORM_RTOL * np.maximum(np.abs(oaux), 1e-30))
         gv = c.v_codes[pg, :, t].reshape(-1, d).astype(np.int64)
-        vm = gv != ev["codes"]
-        assert not (vm & ~_near_threshold(ev["y"], P.vt)).any(), f"slot {slot}: value codes differ"
-        flips += int(vm.sum())
-        gvn = c.v_nu[pg, :, t].reshape(-1).astype(np.float64)
-        assert np.all(np.abs(gvn - ev["nu"]) <= NORM_RTOL * np.maximum(ev["nu"], 1e-30))
+        if cfg.value_mode == "group":
+            assert np.array_equal(gv, ev["codes"]), f"slot {slot}: group value codes differ"
+            assert np.array_equal(c.v_scale[pg, :, t].reshape(ev["scale"].shape).view(np.uint16),
+                                  ev["scale"].view(np.uint16))
+            assert np.array_equal(c.v_zero[pg, :, t].reshape(ev["zero"].shape).view(np.uint16),
+                                  ev["zero"].view(np.uint16))
+        else:
+            vm = gv != ev["codes"]
+            assert not (vm & ~near_threshold(ev["y"], P.vt, P.vt_hi)).any(), f"slot {slot}: value codes differ"
+            flips += int(vm.sum())
+            gvn = c.v_nu[pg, :, t].reshape(-1).astype(np.float64)
+            assert np.all(np.abs(gvn - ev["nu"]) <= NORM_RTOL * np.maximum(ev["nu"], 1e-30))
     return flips
 
 
@@ -165,7 +176,8 @@ def _logit_samples(w, S, cache, bt, slot, rng):
     worst = 0.0
     for g in range(H):
         est = tq.estimate_scores(P, q[g * G:(g + 1) * G], c.k_codes[pg, g, t], c.k_z[pg, g, t], c.k_nu[pg, g, t],
-                                 c.k_gamma[pg, g, t]) / np.sqrt(d)
+                                 c.k_gamma[pg, g, t], c.k_side_idx[pg, g, t], c.k_side_val[pg, g, t],
+                                 c.k_side_cnt[pg, g, t]) / np.sqrt(d)
         got = lg[g * G:(g + 1) * G][:, pos_c]
         scale = np.abs(est).max()
         worst = max(worst, float(np.abs(got - est).max() / scale))
@@ -303,3 +315,13 @@ def test_full_size_mixed_serving_step():
     print(f"[full size] mixed_serving: {sum(len(p) for p in samples.values()) * w.num_kv_heads} sampled "
           f"token-heads ({flips} band flips), decode err {max(errs):.3g}, logit rel err {worst:.3g}", flush=True)
     assert max(errs) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("name", ["mixed_3p5_2p5_decode", "scaled_unbiased_3p5_3_decode", "group_values_decode",
+                                  "outlier_sidecar_decode"])
+def test_full_size_extended_formats(name):
+    """The extended stored formats at their benchmark sizes (256 x 4096, or the
+    outlier workload's 4 x 131072 with a key sidecar), in bench.py's launch
+    configuration; the sidecar workload also reports its quality against exact
+    attention, on the same head as the outlier workload without it."""
+    _full_size_decode(name, head=(2, 5), logit_slot=1, quality=name == "outlier_sidecar_decode")
