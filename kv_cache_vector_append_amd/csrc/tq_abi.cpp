@@ -187,7 +187,7 @@ size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t
   const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, max_ctx > 0 ? max_ctx : 1);
   const size_t partials =
       size_t(num_seqs) * cfg->num_q_heads * (p.splits + 1) * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
-  return tqi::decode_prep_bytes(cfg->head_dim, num_seqs, cfg->num_kv_heads) + partials;
+  return tqi::decode_prep_bytes(*cfg, num_seqs) + partials;
 }
 
 }  // extern "C"

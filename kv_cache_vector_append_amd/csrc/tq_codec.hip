@@ -27,8 +27,9 @@
 //   four wavefronts per (sequence, kv head, context split), one lane per token
 //   for the scores (codebook lookups per coordinate), one thread per
 //   coordinate for the values; a log-sum-exp merge and the inverse value
-//   rotation per query head.  Also the default format's decode where the
-//   matrix-core kernel does not apply (head_dim 64, GQA groups above 4).
+//   rotation per query head.  Used where the matrix-core kernels
+//   (tq_decode_mfma.hip) do not apply: group-quantized values, head_dim 64,
+//   GQA groups above 4.
 // dequant_codec_kernel: one wavefront per (token, kv head).
 #include "tq_device.h"
 
@@ -46,18 +47,6 @@ __host__ __device__ constexpr int table_offset(int kind, int half) {
   return (kind == 0 ? kOffKeyCentroids : kind == 1 ? kOffKeyThresholds : kind == 2 ? kOffValueCentroids
                                                                                    : kOffValueThresholds) +
          (half ? kOffUpperHalf : 0);
-}
-
-// Word offset of 32-coordinate group g inside a key token row.
-__device__ __forceinline__ int key_group_word(const Codec& k, int g, int D) {
-  const int hg = D / (2 * kGroup), lo = k.kbits[0] + k.qjl;
-  return g < hg ? g * lo : hg * lo + (g - hg) * (k.kbits[1] + k.qjl);
-}
-
-// Word offset of coordinate pair i (coordinates 2i, 2i + 1) inside a value block.
-__device__ __forceinline__ int value_pair_word(const Codec& k, int i, int D) {
-  const int hp = D / 4;
-  return i < hp ? i * k.vbits[0] : hp * k.vbits[0] + (i - hp) * k.vbits[1];
 }
 
 // idx = #{j : t_j < y} over the n thresholds (ties to the lower cell)

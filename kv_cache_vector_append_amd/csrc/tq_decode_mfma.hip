@@ -1,12 +1,18 @@
 // Decode attention over the compressed cache on the matrix cores (gfx950).
 //
-// Same computation as the plain kernel in tq_decode.hip ([Design Study] =
+// Same computation as the plain kernel in tq_codec.hip ([Design Study] =
 // "TurboQuant Family Design Study for CPU and Browser WASM KV Caches",
 // "Capacity model" and "CPU and WASM kernel design"; [Reconstruction] =
 // "Mathematical Reconstruction, Lineage, and Accuracy Limits of TurboQuant and
 // TurboVec", section 6 "The Asymmetric Unbiased Estimator"):
 //   est_t = nu_t (<qt, c_K[idx_t]> + gamma_t sqrt(pi/2)/d <qh, 1 - 2 z_t>)
 //   acc_rot = sum_t softmax_t nu_V,t c_V[idx_V,t],  out = T_V^T acc_rot (+ window)
+// The EXT variants take the extended stored formats with Lloyd-Max values
+// (a Codec describes them): per-half bit counts and codebooks ([Design Study]
+// "Packed format and complete bit accounting"), keys scored as
+// s <qt, c_K[idx]> without the QJL plane ([Reconstruction] "The DRIVE/EDEN
+// Mathematical Critique", "12. TurboVec Additions and Divergences"), and the
+// key outlier sidecar, whose sum_j q[idx_j] val_j joins each score.
 // with both contractions on v_mfma_scale_f32_16x16x128_f8f6f4 (tq_mfma.h):
 //
 //   scores^T [16 (head, part) x 16 tokens] = Q [16 x 128 coords, fp8] x planes [128 coords x 16 tokens, fp4]
@@ -49,8 +55,12 @@ __host__ __device__ constexpr int odd_subset(int bits, int i) {
 }
 __host__ __device__ constexpr int num_planes(int bits) { return 1 << (bits - 1); }
 
-// bytes of one (sequence, kv head) entry of the query-operand region
-__host__ __device__ constexpr int prep_stride(int d, int mk) { return (num_planes(mk) + 1) * (d / 128) * 2048 + 256; }
+// bytes of one (sequence, kv head) entry of the query-operand region: the
+// operand images, 256 bytes of scales and constants, and (EXT) the unrotated
+// query of each head for the sidecar entries, as floats in logit units
+__host__ __device__ constexpr int prep_stride(int d, int mk, bool ext) {
+  return (num_planes(mk) + 1) * (d / 128) * 2048 + 256 + (ext ? 4 * kMaxG * d : 0);
+}
 
 template <int BITS>
 __device__ __forceinline__ uint32_t plane_word(const uint32_t* w, int i) {
@@ -152,6 +162,25 @@ __device__ __forceinline__ void load_dwords(const uint32_t* p, bool ok, uint32_t
   }
 }
 
+// N consecutive dwords from global memory at a 4-byte aligned address (the
+// extended layouts place groups and pairs at any word)
+template <int N>
+__device__ __forceinline__ void load_words_a4(const uint8_t* p, uint32_t* out) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4), aligned(4)));
+  typedef uint32_t u2 __attribute__((ext_vector_type(2), aligned(4)));
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    const u4 v = *reinterpret_cast<const u4*>(p + 16 * q);
+    out[4 * q] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
+  }
+  constexpr int Q = N / 4 * 4;
+  if constexpr (N % 4 >= 2) {
+    const u2 v = *reinterpret_cast<const u2*>(p + 4 * Q);
+    out[Q] = v.x; out[Q + 1] = v.y;
+  }
+  if constexpr (N % 2 == 1) out[N - 1] = *reinterpret_cast<const uint32_t*>(p + 4 * (N - 1));
+}
+
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 template <int NW>
@@ -191,19 +220,28 @@ __device__ void check_sequence(const DecodeArgs& a, int s, int tid, int nthreads
 // head h of the GQA group in registers (FWHT variant) and reduces its operand
 // scale and affine constants; then the lane-major operand images are built in
 // LDS and copied out in 16-byte pieces.
-template <int D, int MK, int ROT>
+// EXT: each half of the coordinates takes its own plane coefficients (zero
+// for products of planes the half does not store), the sketch is skipped for
+// scale-corrected keys, and the unrotated query is stored for the sidecar.
+template <int D, int MK, int ROT, bool EXT>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   constexpr int KP = num_planes(MK), KH = D / 128, R = D / 64, T = 256;
   static_assert(T == 64 * kMaxG, "one wavefront per query head of the group");
   __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
   __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
-  __shared__ float coef_k[16], qscale[kMaxG];
+  __shared__ float coef_k[EXT ? 32 : 16], qscale[kMaxG];  // EXT: lower half [0, 16), upper [16, 32)
   __shared__ __attribute__((aligned(16))) uint8_t img[(KP + 1) * KH * 2048];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.cache.num_kv_heads;
   const int G = a.num_q_heads / H;
   const int s = blockIdx.x / H, hk = blockIdx.x % H;
-  uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK);
+  uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
+  float* dst_raw = reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048 + 256);  // EXT only
+  const bool qjl = !EXT || a.cache.codec.qjl;
+  auto load_coef = [&]() {
+    if (tid < (EXT ? 32 : 16))
+      coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
+  };
   if (a.cache.status != nullptr && hk == 0) check_sequence(a, s, tid, T);
   // scores come out in base-2 logits: the softmax scale times log2(e) rides on
   // both query operands, and the QJL constant sqrt(pi/2)/d on the sketch one
@@ -238,7 +276,11 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
       sg1[r] = sign_bit(a.params, kRoleSketch1, c);
       sg2[r] = sign_bit(a.params, kRoleSketch2, c);
     }
-    if (tid < 16) coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef)[tid];
+    load_coef();
+    if constexpr (EXT) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) dst_raw[wv * D + r * 64 + lane] = x[r] * s2;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sgk[r]);
     wave_fwht<R>(x, lane);
@@ -247,10 +289,15 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
       x[r] *= rsqrtf(float(D));
       y[r] = apply_sign(x[r], sg1[r]);
     }
-    wave_fwht<R>(y, lane);
+    if (qjl) {
+      wave_fwht<R>(y, lane);
 #pragma unroll
-    for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
-    wave_fwht<R>(y, lane);
+      for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
+      wave_fwht<R>(y, lane);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) y[r] = 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       q_rot[wv * D + r * 64 + lane] = x[r] * s2;
@@ -260,10 +307,11 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   } else {
     // qt = Pi_K q;  qh = G qt.  Thread i computes row i for the whole group,
     // streaming the row in 16-byte pieces (each matrix entry is read once).
-    if (tid < 16) coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef)[tid];
+    load_coef();
     for (int i = tid; i < kMaxG * D; i += T) {
       const int g = i / D;
       q_rot[i] = g < G ? load_elem(a.q, a.q_dtype, qrow0 * D + i) : 0.f;
+      if constexpr (EXT) dst_raw[i] = q_rot[i] * s2;
     }
     __syncthreads();
     const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
@@ -288,7 +336,11 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     __syncthreads();
     for (int i = tid; i < kMaxG * D; i += T) q_rot[i] = q_sk[i];
     __syncthreads();
-    gemv(pik + size_t(D) * D, q_rot, q_sk);
+    if (qjl) {
+      gemv(pik + size_t(D) * D, q_rot, q_sk);
+    } else {
+      for (int i = tid; i < kMaxG * D; i += T) q_sk[i] = 0.f;
+    }
     __syncthreads();
     for (int i = tid; i < kMaxG * D; i += T) {
       q_rot[i] *= s2;
@@ -306,22 +358,28 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   // [0, 16) E8M0 scales of rows 4 h + p; float [16, 20) key-plane constants,
   // [20, 24) QJL constants.
   {
-    float csum = 0.f, cmax = 0.f;
+    // per half (one half unless EXT): the sum and the largest magnitude of
+    // the plane coefficients
+    float csum[2] = {0.f, 0.f}, cmax[2] = {0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      csum += coef_k[odd_subset(MK, i)];
-      cmax = fmaxf(cmax, fabsf(coef_k[odd_subset(MK, i)]));
-    }
+    for (int hf = 0; hf < (EXT ? 2 : 1); ++hf)
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const float cf = coef_k[16 * hf + odd_subset(MK, i)];
+        csum[hf] += cf;
+        cmax[hf] = fmaxf(cmax[hf], fabsf(cf));
+      }
     float qm = 0.f, qh = 0.f, sm = 0.f, sh = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int c = r * 64 + lane;
+      const int hf = EXT && c >= D / 2 ? 1 : 0;
       const float f = fabsf(fp4_affine_factor(c & 3));
       const float xr = q_rot[wv * D + c], xs = q_sk[wv * D + c];
-      qm = fmaxf(qm, f * fabsf(xr));
+      qm = fmaxf(qm, f * fabsf(xr) * (EXT ? cmax[hf] : 1.f));
       qh = fmaxf(qh, f * fabsf(xs));
       if ((c & 3) != 3) {
-        sm += xr;
+        sm += EXT ? xr * csum[hf] : xr;
         sh += xs;
       }
     }
@@ -329,14 +387,14 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     qh = wave_max(qh);
     sm = wave_sum(sm);
     sh = wave_sum(sh);
-    const int e = fp8_range_exp(fmaxf(qm * cmax, qh));
+    const int e = fp8_range_exp(fmaxf(EXT ? qm : qm * cmax[0], qh));
     if (lane == 0) {
       qscale[wv] = ldexpf(1.f, e);
       int32_t* tail_i = reinterpret_cast<int32_t*>(dst + (KP + 1) * KH * 2048);
       float* tail_f = reinterpret_cast<float*>(tail_i + 16);
 #pragma unroll
       for (int p = 0; p < 4; ++p) tail_i[4 * wv + p] = kScaleOne - e - 4 * p;
-      tail_f[wv] = sm * csum;
+      tail_f[wv] = EXT ? sm : sm * csum[0];
       tail_f[kMaxG + wv] = sh;
     }
   }
@@ -351,7 +409,8 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     const int pl = i / (kMaxG * D / 2), rem = i % (kMaxG * D / 2), h = rem / (D / 2), cp = rem % (D / 2);
     const int c = 8 * (cp >> 2) + (cp & 3);
     const float* src = (pl < KP ? q_rot : q_sk) + h * D;
-    const float mul = fp4_affine_factor(c & 3) * qscale[h] * (pl < KP ? coef_k[odd_subset(MK, pl)] : 1.f);
+    const int chf = EXT && c >= D / 2 ? 16 : 0;
+    const float mul = fp4_affine_factor(c & 3) * qscale[h] * (pl < KP ? coef_k[chf + odd_subset(MK, pl)] : 1.f);
     uint32_t lo, hi;
     fp8_split4_pair(src[c] * mul, src[c + 4] * mul, 0u, 0u, lo, hi);
     const int wd = c / 32;
@@ -567,15 +626,19 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // Two wavefronts per SIMD leave 256.
 constexpr int kRegBudget = 256;
 constexpr int kRegMargin = 68;
-__host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds) {
+// (EXT adds two sidecar words per scored page, the lanes' word offsets and
+// the format's runtime fields.)
+constexpr int kExtMargin = 40;
+__host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds, bool ext = false) {
   return num_planes(BV) * (D / 16 / NW) * 4 + (q_in_lds ? 0 : (num_planes(MK) + 1) * (D / 128) * 8) +
-         (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + kRegMargin;
+         (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + kRegMargin +
+         (ext ? 2 * (8 / NW) + kExtMargin + (MK == 4 ? kExtMargin : 0) : 0);
 }
 __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
   return (D / 16) % NW == 0 && 8 % NW == 0 && ((D / 16) / NW) % 2 == 0;
 }
-__host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds) {
-  return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds) <= kRegBudget;
+__host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds, bool ext = false) {
+  return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds, ext) <= kRegBudget;
 }
 // Wavefronts resident per SIMD.  With three or four value bits at d = 128 the
 // work of a block divides over four wavefronts that each fit in 168 registers
@@ -584,22 +647,23 @@ __host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, boo
 // SIMD: at d = 128 with at most two value bits one wavefront per work item
 // measured faster than four at four per SIMD, whose recent-token window then
 // runs on one of the four.
-__host__ __device__ constexpr int split_occupancy(int D, int MK, int BV) {
-  return D == 128 && BV > 2 ? 3 : 2;
+__host__ __device__ constexpr int split_occupancy(int D, int MK, int BV, bool ext = false) {
+  return D == 128 && BV > 2 && !ext ? 3 : 2;
 }
 // Variants where the estimate above is too optimistic (the compiled loop
 // spills at the estimated count) and the wavefront count that compiles clean.
-__host__ __device__ constexpr int split_waves_override(int D, int MK, int BV) {
-  return split_occupancy(D, MK, BV) > 2 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
+__host__ __device__ constexpr int split_waves_override(int D, int MK, int BV, bool ext = false) {
+  return split_occupancy(D, MK, BV, ext) > 2 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
 }
 // wavefronts per work item: the fewest whose registers fit two wavefronts per SIMD
-__host__ __device__ constexpr int split_waves(int D, int MK, int BV) {
-  return split_waves_override(D, MK, BV) ? split_waves_override(D, MK, BV)
-       : split_fits(D, MK, BV, 1, true) ? 1 : split_fits(D, MK, BV, 2, true) ? 2 : split_fits(D, MK, BV, 4, true) ? 4 : 8;
+__host__ __device__ constexpr int split_waves(int D, int MK, int BV, bool ext = false) {
+  return split_waves_override(D, MK, BV, ext) ? split_waves_override(D, MK, BV, ext)
+       : split_fits(D, MK, BV, 1, true, ext) ? 1 : split_fits(D, MK, BV, 2, true, ext) ? 2
+       : split_fits(D, MK, BV, 4, true, ext) || !split_shape_ok(D, 8) ? 4 : 8;
 }
 // query operands stay in registers when they fit, else each MFMA reads them from LDS
-__host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV) {
-  return split_occupancy(D, MK, BV) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV), false);
+__host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV, bool ext = false) {
+  return split_occupancy(D, MK, BV, ext) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV, ext), false, ext);
 }
 
 // Re-base a head's reference maximum only when a block's maximum exceeds it by
@@ -607,7 +671,14 @@ __host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV) {
 constexpr float kRebase = 28.f;  // base-2 logits: weights stay below 2^28 of the reference
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, int MK, int BV, int NW, bool QL, int OCC>
+// EXT (the extended formats with Lloyd-Max values; MK and BV are the larger
+// half's bit counts): lanes read their key groups and value pairs at the
+// Codec's word offsets, lanes of the lower half (lane groups 0-1 of the
+// scores, coordinate rows 0-7 of the values) ignore the planes they do not
+// store (their plane coefficients are zero), the QJL plane is each group's
+// last, scale-corrected keys skip it, and sidecar records are staged in LDS
+// and added to the scores.
+template <int D, int MK, int BV, int NW, bool QL, int OCC, bool EXT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
   constexpr int KP = num_planes(MK);   // key plane products
   constexpr int VP = num_planes(BV);   // value plane products
@@ -629,6 +700,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   __shared__ __attribute__((aligned(16))) uint8_t q_img[QL ? (KP + 1) * KH * 2048 : 16];  // query operands
   __shared__ float red[NW][8];
   __shared__ float fin[NW][kMaxG];
+  constexpr int kSideWords = 8;  // record stride in LDS: two words per lane group
+  static_assert((1 + kMaxOutliers + 1 + 2 * kMaxOutliers + 3) / 4 <= kSideWords, "sidecar record");
+  __shared__ float q_raw[EXT ? kMaxG * D : 1];                        // unrotated queries (sidecar)
+  __shared__ uint32_t side_lds[EXT ? 8 * kPage * kSideWords : 1];     // the block's sidecar records
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wvu = NW > 1 ? uniform(wv) : 0;  // wavefront index as a scalar
@@ -655,7 +730,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   const int t_end = min(nc, t_begin + a.split_tokens);
 
   // query operands of this (sequence, kv head), lane-major images
-  const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK);
+  const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
+  const Codec& cd = cv.codec;
+  const bool qjl = !EXT || cd.qjl;
+  const int n_side = EXT ? cd.outliers : 0;          // sidecar entries per record
+  const int side_words = EXT ? cd.side_bytes / 4 : 0;
+  if constexpr (EXT) {
+    if (n_side > 0) {
+      const float* src = reinterpret_cast<const float*>(qp + (KP + 1) * KH * 2048 + 256);
+      for (int i = tid; i < kMaxG * D; i += 64 * NW) q_raw[i] = src[i];
+    }
+    if constexpr (!QL) __syncthreads();  // (with QL the operand images' barrier below covers it)
+  }
   v8i qa[QL ? 1 : KP + 1][QL ? 1 : KH];
   if constexpr (QL) {
     for (int i = tid; i < (KP + 1) * KH * 128; i += 64 * NW)
@@ -696,10 +782,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   const uint8_t* kbase = cv.k_pages + size_t(hk) * cv.key_block;
   const uint8_t* vbase = cv.v_pages + size_t(hk) * cv.value_block;
   const size_t kstride = size_t(H) * cv.key_block, vstride = size_t(H) * cv.value_block;
-  const uint32_t k_off = uint32_t((r16 * (D / 32) + KH * g4) * (MK + 1) * 4);
-  const uint32_t kn_off = uint32_t(kcode_bytes + 8 * r16);
-  const uint32_t vn_off = uint32_t(vcode_bytes + 4 * r16);
-  const uint32_t v_off = uint32_t(((NCB * r16 + CBW * wvu) / 2) * BV * 4);
+  uint32_t k_off = uint32_t((r16 * (D / 32) + KH * g4) * (MK + 1) * 4);
+  uint32_t k_off1 = k_off + (MK + 1) * 4;  // second 32-coordinate group of the lane (d = 256)
+  uint32_t kn_off = uint32_t(kcode_bytes + 8 * r16);
+  uint32_t vn_off = uint32_t(vcode_bytes + 4 * r16);
+  uint32_t v_off = uint32_t(((NCB * r16 + CBW * wvu) / 2) * BV * 4);
+  uint32_t v_pair = 0;      // EXT: bytes between the lane's consecutive value pairs
+  int q_word = MK;          // EXT: the lane's QJL word among its group's words
+  uint32_t side_off = 0;    // EXT: this lane's word of its token's sidecar record
+  if constexpr (EXT) {
+    const int kh = g4 >= 2 ? 1 : 0;  // score lane groups 2-3 hold upper-half coordinates
+    const int vh = r16 >= 8 ? 1 : 0;  // value rows 8-15 likewise
+    k_off = uint32_t((r16 * cd.key_row_words + key_group_word(cd, KH * g4, D)) * 4);
+    k_off1 = uint32_t((r16 * cd.key_row_words + key_group_word(cd, KH * g4 + (KH - 1), D)) * 4);
+    kn_off = uint32_t(cd.key_norm_off + 8 * r16);
+    vn_off = uint32_t(cd.value_tail_off + 4 * r16);
+    v_off = uint32_t(value_pair_word(cd, (NCB * r16 + CBW * wvu) / 2, D) * 4);
+    v_pair = uint32_t(cd.vbits[vh] * 4);
+    q_word = cd.kbits[kh];
+    side_off = uint32_t(cd.key_side_off + r16 * cd.side_bytes + 4 * g4);
+  }
   typedef const int __attribute__((address_space(4))) const_int;
   const const_int* bt = (const const_int*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
   // Physical pages of the 8 pages of the block starting at tb (-1 outside
@@ -747,6 +849,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   uint32_t kw[PPW][KW];
   float2 kn[PPW];
   float vn[PPW];
+  uint32_t sw[EXT ? PPW : 1][2];  // EXT: sidecar words g4 and g4 + 4 of the lane's token record
   uint32_t vw[2][VW];  // value words of the block
   auto load_key_page = [&](int j) {
     kid[j] = checked(nkid[j]);
@@ -757,9 +860,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     // loads take the scalar-base addressing form (no 64-bit vector adds)
     uint32_t ko = k_off, kno = kn_off, vno = vn_off;
     asm volatile("" : "+v"(ko), "+v"(kno), "+v"(vno));
-    load_words<KW>(kb + ko, kw[j]);
+    if constexpr (EXT) {
+      uint32_t ko1 = k_off1, so = side_off;
+      asm volatile("" : "+v"(ko1), "+v"(so));
+      load_words_a4<MK + 1>(kb + ko, kw[j]);
+      if constexpr (KH == 2) load_words_a4<MK + 1>(kb + ko1, kw[j] + (MK + 1));
+      if (n_side > 0) {
+        sw[j][0] = g4 < side_words ? *reinterpret_cast<const uint32_t*>(kb + so) : 0u;
+        sw[j][1] = g4 + 4 < side_words ? *reinterpret_cast<const uint32_t*>(kb + so + 16) : 0u;
+      }
+    } else {
+      load_words<KW>(kb + ko, kw[j]);
+    }
     kn[j] = *reinterpret_cast<const float2*>(kb + kno);
     vn[j] = *reinterpret_cast<const float*>(vb + vno);
+  };
+  // The lane's QJL word among the words of its group (EXT: after the
+  // half's own planes), selected with per-lane masks (a select on the word's
+  // index would become an indexed load from scratch memory)
+  uint32_t q_mask[EXT ? MK + 1 : 1];
+  if constexpr (EXT) {
+#pragma unroll
+    for (int p = 0; p <= MK; ++p) {
+      q_mask[p] = q_word == p ? ~0u : 0u;
+      asm volatile("" : "+v"(q_mask[p]));
+    }
+  }
+  auto qjl_word = [&](const uint32_t* w) -> uint32_t {
+    if constexpr (!EXT) {
+      return w[MK];
+    } else {
+      uint32_t z = w[0] & q_mask[0];
+#pragma unroll
+      for (int p = 1; p <= MK; ++p) z |= w[p] & q_mask[p];
+      return z;
+    }
+  };
+  // sum_j q[idx_j] val_j over the sidecar record of token r16 of page j of the
+  // wavefront, for head g4 (logit units), from the records staged in LDS
+  auto side_term = [&](int j) -> float {
+    const uint8_t* rec =
+        reinterpret_cast<const uint8_t*>(side_lds + ((wvu * PPW + j) * kPage + r16) * kSideWords);
+    const int cnt = rec[0];
+    float acc = 0.f;
+    for (int e = 0; e < n_side; ++e) {
+      const int c = rec[1 + e] & (D - 1);
+      const float v = f16_bits_to_float(*reinterpret_cast<const uint16_t*>(rec + cd.side_val_off + 2 * e));
+      acc = e < cnt ? fmaf(q_raw[g4 * D + c], v, acc) : acc;
+    }
+    return acc;
   };
   auto load_keys = [&]() {
 #pragma unroll
@@ -777,7 +926,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       mine = g4 == 1 ? p1 : mine;
       mine = g4 == 2 ? p2 : mine;
       mine = g4 == 3 ? p3 : mine;
-      load_words<VW>(vbase + size_t(mine) * vstride + v_off, vw[hp]);
+      if constexpr (EXT) {
+        const uint8_t* vb = vbase + size_t(mine) * vstride + v_off;
+#pragma unroll
+        for (int cp = 0; cp < CBW / 2; ++cp) load_words_a4<BV>(vb + cp * v_pair, vw[hp] + cp * BV);
+      } else {
+        load_words<VW>(vbase + size_t(mine) * vstride + v_off, vw[hp]);
+      }
     }
   };
 
@@ -802,6 +957,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 #pragma unroll
     for (int j = 0; j < PPW; ++j) kok[j] = kid[j] >= 0;
     float loc_max = -INFINITY, loc_vmax = 0.f;
+    if constexpr (EXT) {
+      // this block's sidecar records to LDS (each wavefront its own pages;
+      // read back by the same wavefront, in order)
+      if (n_side > 0) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+          uint32_t* rec = side_lds + ((wvu * PPW + j) * kPage + r16) * kSideWords;
+          rec[g4] = sw[j][0];
+          rec[g4 + 4] = sw[j][1];
+        }
+      }
+    }
     // plane products x pages: with the query operands in LDS, each operand is
     // read once per block and feeds one independent MFMA per page; with them
     // in registers, page by page (pages interleave across the chains)
@@ -816,6 +983,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       for (int hf = 0; hf < KH; ++hf)
 #pragma unroll
         for (int pl = 0; pl <= KP; ++pl) {
+          if (pl == KP && !qjl) break;
           const v8i qo = qop(pl, hf);
 #pragma unroll
           for (int j = 0; j < PPW; ++j) {
@@ -823,7 +991,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
             if (pl < KP)
               dm[j] = mfma_f8_f4(qo, bits_to_fp4_affine(plane_word<MK>(w, pl)), dm[j], sa);
             else
-              dq[j] = mfma_f8_f4(qo, bits_to_fp4_affine(w[MK]), dq[j], sa);
+              dq[j] = mfma_f8_f4(qo, bits_to_fp4_affine(qjl_word(w)), dq[j], sa);
           }
         }
     }
@@ -838,7 +1006,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 #pragma unroll
           for (int pl = 0; pl < KP; ++pl)
             dm[j] = mfma_f8_f4(qop(pl, hf), bits_to_fp4_affine(plane_word<MK>(w, pl)), dm[j], sa);
-          dq[j] = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(w[MK]), dq[j], sa);
+          if (qjl) dq[j] = mfma_f8_f4(qop(KP, hf), bits_to_fp4_affine(qjl_word(w)), dq[j], sa);
         }
         // this page's registers are consumed: request the next block's page
         // now, so that the wavefront's key requests stay spread over the
@@ -849,7 +1017,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       // dm[i], dq[i]: part i of head g4 for token r16, already in logit units
       const float msum = (dm[j][0] + dm[j][1]) + (dm[j][2] + dm[j][3]);
       const float qsum = (dq[j][0] + dq[j][1]) + (dq[j][2] + dq[j][3]);
-      const float est = knj.x * fmaf(knj.y, qsum, msum);
+      float est = knj.x * fmaf(knj.y, qsum, msum);
+      if constexpr (EXT) {
+        if (!qjl) est = knj.y * msum;  // s <qt, c[idx]>
+        if (n_side > 0) est += side_term(j);
+      }
       const bool tok_ok = pos < t_end && kok[j];
       const bool valid = tok_ok && head_ok;
       sc[j] = valid ? est : -INFINITY;
@@ -969,7 +1141,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   }
 
   // ------------------------------------------------------------ partial results
-  const float* coef_v = reinterpret_cast<const float*>(a.params + kOffValuePlaneCoef);
+  // (EXT: lane groups 2-3 hold upper-half coordinates, with their own coefficients)
+  const float* coef_v =
+      reinterpret_cast<const float*>(a.params + kOffValuePlaneCoef + (EXT && g4 >= 2 ? kOffUpperHalf : 0));
   const float l_w = sum16(l_part);
   float l = l_w;
   if constexpr (NW > 1) {
@@ -1170,18 +1344,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
   }
 }
 
-template <int D, int MK, int BV, int ROT>
-hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
-  constexpr int NW = split_waves(D, MK, BV);
-  constexpr bool QL = split_q_in_lds(D, MK, BV);
-  constexpr int OCC = split_occupancy(D, MK, BV);
+template <int D, int MK, int BV, int ROT, bool EXT>
+hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) {
+  constexpr int NW = split_waves(D, MK, BV, EXT);
+  constexpr bool QL = split_q_in_lds(D, MK, BV, EXT);
+  constexpr int OCC = split_occupancy(D, MK, BV, EXT);
   const int H = a.cache.num_kv_heads;
-  const size_t part_offset = decode_prep_bytes(D, a.num_seqs, H);
-  hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT>), dim3(a.num_seqs * H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW), 0, st,
-                     a, part_offset);
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW),
+                     0, st, a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
@@ -1196,14 +1369,26 @@ hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int ROT>
-hipError_t dispatch_bits(const DecodeArgs& a, hipStream_t st) {
-  const int mk = a.key_mse_bits, bv = a.value_bits;
+// Key and value bit counts the kernels are built for: the larger half's
+// (the default format has one count per role).
+struct Bits {
+  int mk, bv;
+};
+Bits kernel_bits(const tq_config& cfg) {
+  const Codec k = make_codec(cfg);
+  return {k.kbits[0] > k.kbits[1] ? k.kbits[0] : k.kbits[1], k.vbits[0] > k.vbits[1] ? k.vbits[0] : k.vbits[1]};
+}
+
+template <int D, int ROT, bool EXT>
+hipError_t dispatch_bits(const DecodeArgs& a, Bits b, size_t part_offset, hipStream_t st) {
 #define TQ_CASE(MK_, BV_) \
-  if (mk == MK_ && bv == BV_) return launch_mfma<D, MK_, BV_, ROT>(a, st);
+  if (b.mk == MK_ && b.bv == BV_) return launch_mfma<D, MK_, BV_, ROT, EXT>(a, part_offset, st);
   TQ_CASE(1, 1) TQ_CASE(1, 2) TQ_CASE(1, 3) TQ_CASE(1, 4)
   TQ_CASE(2, 1) TQ_CASE(2, 2) TQ_CASE(2, 3) TQ_CASE(2, 4)
   TQ_CASE(3, 1) TQ_CASE(3, 2) TQ_CASE(3, 3) TQ_CASE(3, 4)
+  if constexpr (EXT) {  // all four key bits to the codebook (scale-corrected keys)
+    TQ_CASE(4, 1) TQ_CASE(4, 2) TQ_CASE(4, 3) TQ_CASE(4, 4)
+  }
 #undef TQ_CASE
   return hipErrorInvalidValue;
 }
@@ -1211,36 +1396,46 @@ hipError_t dispatch_bits(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 int decode_mfma_items(const tq_config& cfg) {
-  const int d = cfg.head_dim, mk = cfg.key_bits - 1, bv = cfg.value_bits;
-  if (mk < 1 || mk > 3 || bv < 1 || bv > 4 || (d != 128 && d != 256)) return 2048;
+  const Bits b = kernel_bits(cfg);
+  const int d = cfg.head_dim;
+  if (b.mk < 1 || b.mk > 4 || b.bv < 1 || b.bv > 4 || (d != 128 && d != 256)) return 2048;
   // work items that fill every SIMD once: 1024 SIMDs x resident wavefronts / wavefronts per item
-#define TQ_ITEMS(D_, MK_, BV_) (1024 * split_occupancy(D_, MK_, BV_) / split_waves(D_, MK_, BV_))
-  constexpr int i128[3][4] = {{TQ_ITEMS(128, 1, 1), TQ_ITEMS(128, 1, 2), TQ_ITEMS(128, 1, 3), TQ_ITEMS(128, 1, 4)},
-                              {TQ_ITEMS(128, 2, 1), TQ_ITEMS(128, 2, 2), TQ_ITEMS(128, 2, 3), TQ_ITEMS(128, 2, 4)},
-                              {TQ_ITEMS(128, 3, 1), TQ_ITEMS(128, 3, 2), TQ_ITEMS(128, 3, 3), TQ_ITEMS(128, 3, 4)}};
-  constexpr int i256[3][4] = {{TQ_ITEMS(256, 1, 1), TQ_ITEMS(256, 1, 2), TQ_ITEMS(256, 1, 3), TQ_ITEMS(256, 1, 4)},
-                              {TQ_ITEMS(256, 2, 1), TQ_ITEMS(256, 2, 2), TQ_ITEMS(256, 2, 3), TQ_ITEMS(256, 2, 4)},
-                              {TQ_ITEMS(256, 3, 1), TQ_ITEMS(256, 3, 2), TQ_ITEMS(256, 3, 3), TQ_ITEMS(256, 3, 4)}};
-#undef TQ_ITEMS
-  return d == 128 ? i128[mk - 1][bv - 1] : i256[mk - 1][bv - 1];
+  const bool ext = make_codec(cfg).ext != 0;
+  return 1024 * split_occupancy(d, b.mk, b.bv, ext) / split_waves(d, b.mk, b.bv, ext);
 }
 
-size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads) {
-  // sized for the largest key bit width, 256-byte aligned
-  const size_t b = size_t(num_seqs) * num_kv_heads * prep_stride(d, 3);
+size_t decode_prep_bytes(const tq_config& cfg, int num_seqs) {
+  // the default format's region is sized for its largest key bit width; an
+  // extended format's for the bits its kernels are built for; 256-byte aligned
+  const int d = cfg.head_dim;
+  const size_t stride = make_codec(cfg).ext ? prep_stride(d, kernel_bits(cfg).mk, true) : prep_stride(d, 3, false);
+  const size_t b = size_t(num_seqs) * cfg.num_kv_heads * stride;
   return (b + 255) & ~size_t(255);
 }
 
+// The matrix-core path takes head_dim 128 and 256, GQA groups up to 4, and
+// every stored format whose values are Lloyd-Max coded (group-quantized
+// values take the plain kernel).
 bool decode_mfma_supported(const tq_config& cfg) {
   return (cfg.head_dim == 128 || cfg.head_dim == 256) && cfg.num_q_heads / cfg.num_kv_heads <= kMaxG &&
-         cfg.page_tokens == kPage && cfg.window <= 1024 && !make_codec(cfg).ext;
+         cfg.page_tokens == kPage && cfg.window <= 1024 && cfg.value_mode == TQ_VALUE_LLOYD;
 }
 
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool dense = cfg.rotation == TQ_ROT_DENSE;
-  if (cfg.head_dim == 128) return dense ? dispatch_bits<128, TQ_ROT_DENSE>(a, st) : dispatch_bits<128, TQ_ROT_FWHT>(a, st);
-  if (cfg.head_dim == 256) return dense ? dispatch_bits<256, TQ_ROT_DENSE>(a, st) : dispatch_bits<256, TQ_ROT_FWHT>(a, st);
+  const bool ext = make_codec(cfg).ext != 0;
+  const Bits b = kernel_bits(cfg);
+  const size_t part_offset = decode_prep_bytes(cfg, a.num_seqs);
+#define TQ_DISPATCH(D_)                                                                                   \
+  if (cfg.head_dim == D_) {                                                                               \
+    if (ext) return dense ? dispatch_bits<D_, TQ_ROT_DENSE, true>(a, b, part_offset, st)                  \
+                          : dispatch_bits<D_, TQ_ROT_FWHT, true>(a, b, part_offset, st);                  \
+    return dense ? dispatch_bits<D_, TQ_ROT_DENSE, false>(a, b, part_offset, st)                          \
+                 : dispatch_bits<D_, TQ_ROT_FWHT, false>(a, b, part_offset, st);                          \
+  }
+  TQ_DISPATCH(128) TQ_DISPATCH(256)
+#undef TQ_DISPATCH
   return hipErrorInvalidValue;
 }
 

@@ -44,6 +44,19 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Word offset of 32-coordinate group g inside a key token row (each group
+// holds its half's code planes, then its QJL plane when there is one).
+__device__ __forceinline__ int key_group_word(const Codec& k, int g, int D) {
+  const int hg = D / (2 * kGroup), lo = k.kbits[0] + k.qjl;
+  return g < hg ? g * lo : hg * lo + (g - hg) * (k.kbits[1] + k.qjl);
+}
+
+// Word offset of coordinate pair i (coordinates 2i, 2i + 1) inside a value block.
+__device__ __forceinline__ int value_pair_word(const Codec& k, int i, int D) {
+  const int hp = D / 4;
+  return i < hp ? i * k.vbits[0] : hp * k.vbits[0] + (i - hp) * k.vbits[1];
+}
+
 // Negate v when bit `bit` of the sign word is set (the Rademacher stage D).
 __device__ __forceinline__ float apply_sign(float v, uint32_t bit) {
   return __uint_as_float(__float_as_uint(v) ^ (bit << 31));

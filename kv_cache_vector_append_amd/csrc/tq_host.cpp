@@ -226,7 +226,7 @@ void write_signs(uint8_t* blob, uint64_t seed, int d) {
 // a whole number of tiles (the matrix-core kernel's 128-token blocks, the
 // plain kernel's 64-token tiles).
 SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
-  const bool mfma = decode_mfma_supported(cfg);  // false for the extended formats
+  const bool mfma = decode_mfma_supported(cfg);
   const int units = (num_seqs > 0 ? num_seqs : 1) * cfg.num_kv_heads;
   const int tile = mfma ? 128 : 64;
   const int items = mfma ? decode_mfma_items(cfg) : 2048;

@@ -167,7 +167,7 @@ int launch_append_codec(const tq_config& cfg, const AppendArgs& a, int num_seqs,
 int launch_decode_codec(const tq_config& cfg, const DecodeArgs& a, void* stream);
 bool decode_mfma_supported(const tq_config& cfg);
 int decode_mfma_items(const tq_config& cfg);  // (sequence, KV head, split) work items that fill the GPU once
-size_t decode_prep_bytes(int d, int num_seqs, int num_kv_heads);  // query-operand region at the workspace start
+size_t decode_prep_bytes(const tq_config& cfg, int num_seqs);  // query-operand region at the workspace start
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream);
 int launch_dequantize_codec(const tq_config& cfg, const DequantArgs& a, void* stream);
 
