@@ -517,8 +517,8 @@ def cpu_baseline(w, reps=4):
 # decode.
 EXTRA_WORKLOADS = ("mixed_serving", "hd256_long_dense_3_2", "hd256_long_dense_4_4", "hd256_dense_prefill",
                    "gqa_decode",
-                   # extended stored formats (the generic path): mixed-channel rates, scaled keys,
-                   # group-quantized values, and the outlier workload with a key sidecar
+                   # extended stored formats: mixed-channel rates, scaled keys, group-quantized
+                   # values, and the outlier workload with a key sidecar
                    "mixed_3p5_2p5_decode", "scaled_unbiased_3p5_3_decode", "group_values_decode",
                    "outlier_sidecar_decode")
 # (sequence, kv head) whose query group the quality metrics cover (the same

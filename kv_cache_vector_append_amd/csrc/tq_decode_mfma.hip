@@ -224,13 +224,20 @@ __device__ void check_sequence(const DecodeArgs& a, int s, int tid, int nthreads
 // for products of planes the half does not store), the sketch is skipped for
 // scale-corrected keys, and the unrotated query is stored for the sidecar.
 template <int D, int MK, int ROT, bool EXT>
-__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
-  constexpr int KP = num_planes(MK), KH = D / 128, R = D / 64, T = 256;
-  static_assert(T == 64 * kMaxG, "one wavefront per query head of the group");
+__global__ __launch_bounds__(ROT == TQ_ROT_DENSE ? 1024 : 256) void decode_prep_kernel(DecodeArgs a) {
+  // FWHT variant: one wavefront per query head; dense variant: 1024 threads,
+  // so that the matrix-vector products have enough wavefronts to hide latency
+  constexpr int KP = num_planes(MK), KH = D / 128, R = D / 64, T = ROT == TQ_ROT_DENSE ? 1024 : 256;
+  constexpr int KQ = T / D;  // dense: slices of the contraction per output row
+  static_assert(T >= 64 * kMaxG, "a wavefront per query head of the group");
+  // operand images; before them (dense variant) the products' partial sums per slice
+  constexpr int kImgBytes = (KP + 1) * KH * 2048;
+  constexpr int kRedBytes = ROT == TQ_ROT_DENSE ? 2 * KQ * kMaxG * D * 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t img[kImgBytes > kRedBytes ? kImgBytes : kRedBytes];
+  float* red = reinterpret_cast<float*>(img);
   __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
   __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
   __shared__ float coef_k[EXT ? 32 : 16], qscale[kMaxG];  // EXT: lower half [0, 16), upper [16, 32)
-  __shared__ __attribute__((aligned(16))) uint8_t img[(KP + 1) * KH * 2048];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.cache.num_kv_heads;
   const int G = a.num_q_heads / H;
@@ -305,8 +312,11 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
     }
     __syncthreads();
   } else {
-    // qt = Pi_K q;  qh = G qt.  Thread i computes row i for the whole group,
-    // streaming the row in 16-byte pieces (each matrix entry is read once).
+    // qt = Pi_K q and qh = G Pi_K q in one pass over q, from the transposed
+    // matrices Pi_K^T and (G Pi_K)^T: thread (i, k) sums slice k of the
+    // products for output coordinate i of the whole group, so that the threads
+    // of a wavefront read consecutive entries of a matrix row (each entry is
+    // read once); the slices meet in LDS.
     load_coef();
     for (int i = tid; i < kMaxG * D; i += T) {
       const int g = i / D;
@@ -314,39 +324,49 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
       if constexpr (EXT) dst_raw[i] = q_rot[i] * s2;
     }
     __syncthreads();
-    const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
-    auto gemv = [&](const float* m, const float* x, float* y) {
-      for (int i = tid; i < D; i += T) {
-        const float4* row = reinterpret_cast<const float4*>(m + size_t(i) * D);
-        float acc[kMaxG] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int j4 = 0; j4 < D / 4; ++j4) {
-          const float4 mv = row[j4];
+    {
+      constexpr int J = D / KQ;  // contraction slice per thread
+      const int i = tid % D, k = tid / D, k0 = k * J;
+      const float* m0 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 0)) + size_t(k0) * D + i;
+      const float* m1 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 1)) + size_t(k0) * D + i;
+      float ar[kMaxG] = {0.f, 0.f, 0.f, 0.f}, as[kMaxG] = {0.f, 0.f, 0.f, 0.f};
+      if (qjl) {
+#pragma unroll 16
+        for (int j = 0; j < J; ++j) {
+          const float u = m0[size_t(j) * D], v = m1[size_t(j) * D];
 #pragma unroll
           for (int h = 0; h < kMaxG; ++h) {
-            const float4 xv = *reinterpret_cast<const float4*>(x + h * D + 4 * j4);
-            acc[h] = fmaf(mv.x, xv.x, fmaf(mv.y, xv.y, fmaf(mv.z, xv.z, fmaf(mv.w, xv.w, acc[h]))));
+            const float x = q_rot[h * D + k0 + j];
+            ar[h] = fmaf(u, x, ar[h]);
+            as[h] = fmaf(v, x, as[h]);
           }
         }
+      } else {
+#pragma unroll 16
+        for (int j = 0; j < J; ++j) {
+          const float u = m0[size_t(j) * D];
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) y[h * D + i] = acc[h];
+          for (int h = 0; h < kMaxG; ++h) ar[h] = fmaf(u, q_rot[h * D + k0 + j], ar[h]);
+        }
       }
-    };
-    gemv(pik, q_rot, q_sk);
-    __syncthreads();
-    for (int i = tid; i < kMaxG * D; i += T) q_rot[i] = q_sk[i];
-    __syncthreads();
-    if (qjl) {
-      gemv(pik + size_t(D) * D, q_rot, q_sk);
-    } else {
-      for (int i = tid; i < kMaxG * D; i += T) q_sk[i] = 0.f;
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        red[(k * kMaxG + h) * D + i] = ar[h];
+        red[((KQ + k) * kMaxG + h) * D + i] = as[h];
+      }
+      __syncthreads();
+      for (int o = tid; o < kMaxG * D; o += T) {
+        float vr = 0.f, vs = 0.f;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          vr += red[q * kMaxG * D + o];
+          vs += red[(KQ + q) * kMaxG * D + o];
+        }
+        q_rot[o] = vr * s2;
+        q_sk[o] = vs * s2q;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = tid; i < kMaxG * D; i += T) {
-      q_rot[i] *= s2;
-      q_sk[i] *= s2q;
-    }
-    __syncthreads();
   }
   // Per head (wavefront wv): one power of two 2^e bringing the larger of its
   // key-plane and QJL operands' largest entry into (128, 256] (the smaller
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   // the coordinates with c % 4 < 3, which seed the accumulators.  Tail: int32
   // [0, 16) E8M0 scales of rows 4 h + p; float [16, 20) key-plane constants,
   // [20, 24) QJL constants.
-  {
+  if (wv < kMaxG) {
     // per half (one half unless EXT): the sum and the largest magnitude of
     // the plane coefficients
     float csum[2] = {0.f, 0.f}, cmax[2] = {0.f, 0.f};
@@ -728,6 +748,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   float* ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + part_offset);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(nc, t_begin + a.split_tokens);
+  // the item after the last split attends the recent-token window, exactly,
+  // from the fp16 ring (first wavefront, in the weight operand's LDS), so that
+  // it runs beside the compressed splits instead of after one of them
+  if (split == a.splits) {
+    if (wv == 0) window_part<D>(a, ws, s, hk, G, slot, nc, L, reinterpret_cast<float*>(w_img));
+    return;
+  }
 
   // query operands of this (sequence, kv head), lane-major images
   const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
@@ -1178,9 +1205,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       const int coord = NCB * (4 * g4 + i) + CBW * wv + c;
       if (cq == 0 && ch < G) wsh[coord] = v;
     }
-  // the recent-token window, exactly, from the fp16 ring: the last split's
-  // first wavefront, in the weight operand's LDS (free after the last block)
-  if (split == a.splits - 1 && wv == 0) window_part<D>(a, ws, s, hk, G, slot, nc, L, reinterpret_cast<float*>(w_img));
 }
 
 // Merge the compressed splits of one (sequence, query head) by log-sum-exp,
@@ -1188,9 +1212,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 // normalise and store.  FWHT variant: one wavefront per row, four rows per
 // workgroup -- the splits' maxima and denominators across lanes, the value
 // sums per coordinate (D / 64 per lane) with several loads in flight, the
-// inverse FWHT in registers.  Dense variant: one row per workgroup, one
-// coordinate per thread, the inverse rotation as a matrix-vector product
-// through LDS.  With few rows (WIDE, FWHT only) one row takes a whole
+// inverse FWHT in registers.  Dense variant: one row per workgroup of 1024
+// threads, D per slice: each slice sums every KQ-th split for its coordinate,
+// then multiplies its share of the rows of Pi_V^T, the slices meeting in LDS
+// (enough wavefronts to hide the loads' latency).  With few rows (WIDE, FWHT only) one row takes a whole
 // workgroup instead: each wavefront sums a quarter of the splits, the partial
 // sums meet in LDS and the first wavefront finishes the row, so that a short
 // list of rows still spreads its record loads over many CUs.
@@ -1201,12 +1226,15 @@ template <int N>
 struct Count {
   static constexpr int value = N;
 };  // FWHT rows up to this many: a workgroup per row
+template <int ROT>
+__host__ __device__ constexpr int combine_threads() { return ROT == TQ_ROT_DENSE ? 1024 : 256; }
 template <int D, int ROT, bool WIDE>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
+__global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(DecodeArgs a, size_t part_offset) {
   static_assert(!WIDE || ROT == TQ_ROT_FWHT, "the wide combine is the FWHT variant's");
   constexpr int R = D / 64;
   constexpr int RPB = WIDE ? 1 : combine_rows<ROT>(0);
-  __shared__ float buf[ROT == TQ_ROT_DENSE ? D : (WIDE ? 4 * D : 1)];
+  constexpr int KQ = combine_threads<ROT>() / D;  // dense: slices of the sums per coordinate
+  __shared__ float buf[ROT == TQ_ROT_DENSE ? (KQ + 1) * D : (WIDE ? 4 * D : 1)];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t row = size_t(blockIdx.x) * RPB + (RPB > 1 ? wv : 0);  // s * H_q + h
   if (RPB > 1 && row >= size_t(a.num_seqs) * a.num_q_heads) return;  // whole wavefronts; no barrier on this path
@@ -1224,10 +1252,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
   const int ns = min(a.splits, (nc + a.split_tokens - 1) / a.split_tokens);
   auto rec_of = [&](int sp) { return ws + size_t(sp < ns ? sp : a.splits) * rec; };  // the window's record last
   // maximum and denominator over the records (every wavefront of the row
-  // alike).  In the wide form with fewer than 64 compressed records, lane sp
-  // keeps record sp's weight (lane ns the window's), and the weights are
-  // broadcast from the lanes instead of being read again.
-  const bool in_lanes = WIDE && ns < 64;
+  // alike).  In the wide and the dense forms with fewer than 64 compressed
+  // records, lane sp keeps record sp's weight (lane ns the window's), and the
+  // weights are broadcast from the lanes instead of being read again (every
+  // caller's split index is uniform across its wavefront).
+  const bool in_lanes = (WIDE || ROT == TQ_ROT_DENSE) && ns < 64;
   float M = -INFINITY, l = 0.f, wl = 0.f;
   if (in_lanes) {
     float m = -INFINITY, lr = 0.f;
@@ -1312,32 +1341,52 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, size_
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
   } else {
-    const int c = tid;
+    // thread (c, k): coordinate c, slice k of the splits and then of the
+    // rows of Pi_V; the slices meet in LDS (buf[k D + c]; the merged sum at
+    // buf[KQ D + c])
+    const int c = tid % D, k = tid / D;
+    constexpr int J = D / KQ;
+    // this thread's share of Pi_V^T, requested before the merge so that its
+    // loads overlap the merge's
+    const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D + size_t(k * J) * D + c;
+    float pv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) pv[j] = piv[size_t(j) * D];
     float ar = 0.f;
-    if (c < D) {
-      int sp = 0;
-      for (; sp + 4 <= ns; sp += 4) {
+    {
+      int sp = k;
+      for (; sp + 3 * KQ < ns; sp += 4 * KQ) {
         float f[4], v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          f[u] = weight(sp + u);
-          v[u] = ws[size_t(sp + u) * rec + 2 + c];
+          f[u] = weight(sp + u * KQ);
+          v[u] = ws[size_t(sp + u * KQ) * rec + 2 + c];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) ar = fmaf(f[u], v[u], ar);
       }
-      for (; sp < ns; ++sp) ar = fmaf(weight(sp), ws[size_t(sp) * rec + 2 + c], ar);
-      buf[c] = ar;
+      for (; sp < ns; sp += KQ) ar = fmaf(weight(sp), ws[size_t(sp) * rec + 2 + c], ar);
+    }
+    buf[k * D + c] = ar;
+    __syncthreads();
+    if (k == 0) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) v += buf[q * D + c];
+      buf[KQ * D + c] = v;
     }
     __syncthreads();
-    if (c < D) {
-      const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D;
-      float o4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8  // 32 matrix rows in flight per thread
-      for (int j = 0; j < D; j += 4)
+    const float* sum = buf + KQ * D + k * J;
+    float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o4[u] = fmaf(piv[size_t(j + u) * D + c], buf[j + u], o4[u]);
-      const float o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+    for (int j = 0; j < J; ++j) o4[j % 4] = fmaf(pv[j], sum[j], o4[j % 4]);
+    __syncthreads();  // every read of the slices above is done
+    buf[k * D + c] = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+    __syncthreads();
+    if (k == 0) {
+      float o = 0.f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) o += buf[q * D + c];
       const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
@@ -1350,11 +1399,13 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
   constexpr bool QL = split_q_in_lds(D, MK, BV, EXT);
   constexpr int OCC = split_occupancy(D, MK, BV, EXT);
   const int H = a.cache.num_kv_heads;
-  hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(ROT == TQ_ROT_DENSE ? 1024 : 256),
+                     0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits), dim3(64 * NW),
-                     0, st, a, part_offset);
+  // one work item per (sequence, kv head, split), plus one per (sequence, kv head) for the window
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits + 1),
+                     dim3(64 * NW), 0, st, a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
@@ -1364,7 +1415,7 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D, ROT, false>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((decode_combine_kernel<D, ROT, false>), dim3((rows + rpb - 1) / rpb), dim3(combine_threads<ROT>()), 0, st, a,
                      part_offset);
   return hipGetLastError();
 }

@@ -5,6 +5,7 @@
 // [Reconstruction] = "Mathematical Reconstruction, Lineage, and Accuracy Limits
 // of TurboQuant and TurboVec"; [Design Study] = "TurboQuant Family Design
 // Study for CPU and Browser WASM KV Caches".
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -299,10 +300,12 @@ void build_params(const tq_config& cfg, uint8_t* blob) {
   if (cfg.rotation == TQ_ROT_DENSE) {
     float* dst = reinterpret_cast<float*>(blob + kOffDense);
     const uint64_t roles[3] = {kKeyGauss, kSketchGauss, kValueGauss};
+    std::vector<double> exact[2];  // Pi_K and G in double, for the query preparation's matrices
     for (int m = 0; m < 3; ++m) {
       std::vector<double> g = gaussian(cfg.seed, roles[m], d, d);
       if (m != 1) g = haar_from_gaussian(std::move(g), d);
       for (size_t i = 0; i < size_t(d) * d; ++i) dst[size_t(m) * d * d + i] = float(g[i]);
+      if (m < 2) exact[m] = g;
       // fp16 hi / lo split of the scaled fp32 matrix for the matrix cores
       _Float16* hi = reinterpret_cast<_Float16*>(blob + dense16_offset(d, m));
       _Float16* lo = hi + size_t(d) * d;
@@ -310,6 +313,24 @@ void build_params(const tq_config& cfg, uint8_t* blob) {
         const float v = dst[size_t(m) * d * d + i] * kDense16Scale[m];
         hi[i] = _Float16(v);
         lo[i] = _Float16(v - float(hi[i]));
+      }
+    }
+    // The query preparation's matrices, transposed: Pi_K^T, and (G Pi_K)^T,
+    // which maps the query straight to its sketch (qh = G Pi_K q), formed in
+    // double and rounded once.
+    float* t0 = reinterpret_cast<float*>(blob + dense_t_offset(d, 0));
+    float* t1 = reinterpret_cast<float*>(blob + dense_t_offset(d, 1));
+    std::vector<double> row(d);
+    for (int r = 0; r < d; ++r) {
+      std::fill(row.begin(), row.end(), 0.0);
+      for (int k = 0; k < d; ++k) {
+        const double gk = exact[1][size_t(r) * d + k];
+        const double* pk = exact[0].data() + size_t(k) * d;
+        for (int c = 0; c < d; ++c) row[c] += gk * pk[c];
+      }
+      for (int c = 0; c < d; ++c) {
+        t0[size_t(c) * d + r] = float(exact[0][size_t(r) * d + c]);
+        t1[size_t(c) * d + r] = float(row[c]);
       }
     }
   }

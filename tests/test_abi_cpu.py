@@ -77,6 +77,11 @@ def test_host_params_match_oracle(d, kb, vb, rot):
             ref = s * M[m].astype(np.float64)
             assert np.array_equal(h16[m, 0], ref.astype(np.float16).astype(np.float64))
             assert np.abs(h16[m, 0] + h16[m, 1] - ref).max() <= 2.0 ** -20 * np.abs(ref).max()
+        # the decode's query preparation: Pi_K^T and (G Pi_K)^T in fp32
+        Mt = f[(2048 + 24 * d * d) // 4:(2048 + 32 * d * d) // 4].reshape(2, d, d).astype(np.float64)
+        assert np.abs(Mt[0] - T.pk.T).max() < 1e-6
+        gp = (T.g @ T.pk).T
+        assert np.abs(Mt[1] - gp).max() <= 2.0 ** -23 * np.abs(gp).max() * 2
 
 
 def test_size_queries_match_layout():
@@ -87,7 +92,7 @@ def test_size_queries_match_layout():
         f = tq.Config(d, 8, 2, kb, vb)
         assert tqa.key_block_bytes(cfg) == layout.key_block_bytes(f)
         assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(f)
-        assert tqa.params_bytes(cfg) == 2048 + (3 * d * d * 8 if rot == "dense" else 0)
+        assert tqa.params_bytes(cfg) == 2048 + (32 * d * d if rot == "dense" else 0)
         ws = tqa.decode_workspace_bytes(cfg, 3, 1000)
         # at least one partial record (max, denominator, d sums) per (sequence, query head)
         # for the compressed part and one for the window, in float32
