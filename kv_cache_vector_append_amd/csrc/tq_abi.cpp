@@ -186,7 +186,8 @@ size_t tq_decode_workspace_bytes(const tq_config* cfg, int32_t num_seqs, int32_t
   if (check_config(cfg) != TQ_OK || num_seqs <= 0 || max_ctx < 0 || max_ctx > TQ_MAX_CONTEXT) return 0;
   const tqi::SplitPlan p = tqi::plan_splits(*cfg, num_seqs, max_ctx > 0 ? max_ctx : 1);
   const size_t partials =
-      size_t(num_seqs) * cfg->num_q_heads * (p.splits + 1) * (2 + 2 * size_t(cfg->head_dim)) * sizeof(float);
+      size_t(num_seqs) * cfg->num_q_heads * (p.splits + tqi::kWindowRecords) * (2 + 2 * size_t(cfg->head_dim)) *
+      sizeof(float);
   return tqi::decode_prep_bytes(*cfg, num_seqs) + partials;
 }
 
@@ -243,6 +244,7 @@ tq_status decode(const tq_config* cfg, const void* params_dev, const tq_cache* c
   a.value_bits = cfg->value_bits;
   a.splits = p.splits;
   a.split_tokens = p.split_tokens;
+  a.window_items = p.window_items;
   a.max_ctx = mc;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
   const int e = tqi::decode_mfma_supported(*cfg) ? tqi::launch_decode_mfma(*cfg, a, stream)

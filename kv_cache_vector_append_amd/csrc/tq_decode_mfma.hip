@@ -451,9 +451,11 @@ __global__ __launch_bounds__(ROT == TQ_ROT_DENSE ? 1024 : 256) void decode_prep_
 // ---------------------------------------------------------------------------- recent-token window
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-// Positions [nc, L) from the fp16 ring, exactly, on one wavefront, with an
-// online softmax over blocks of 16 tokens; writes (max, denominator,
-// sum_t p_t v_t) per query head in the value's own (unrotated) basis.
+// Positions [nc, L) from the fp16 ring, exactly: window item wi (of
+// a.window_items) takes the 16-token blocks wi, wi + window_items, ... on
+// one wavefront, with an online softmax over its blocks, and writes (max,
+// denominator, sum_t p_t v_t) per query head, in the value's own (unrotated)
+// basis, to record splits + wi.
 //   scores: v_mfma_f32_16x16x32_f16 with rows 2h + part holding the query of
 //     head h as two fp16 parts (hi + lo, after a power-of-two scale) and
 //     columns the ring's fp16 keys of 16 tokens, so every product is exact and
@@ -462,17 +464,18 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 //     `pbuf` (64 floats of LDS).
 // Both score operands place coordinate 32 kc + 8 g + e at element e of lane
 // group g of chunk kc, which pairs the same coordinate on both sides whatever
-// the instruction's internal K order.  A block's ring rows are requested one
-// block ahead.
-template <int D>
+// the instruction's internal K order.  A block's ring rows are requested DP
+// blocks ahead.
+template <int D, int DP>
 __device__ void window_part(const DecodeArgs& a, float* ws, int s, int hk, int G, int slot, int nc, int L,
-                            float* pbuf) {
+                            int wi, float* pbuf) {
   constexpr int KC = D / 32, NP = D / 128;
+  const int kStep = 16 * a.window_items;  // tokens between this item's blocks
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads, W = cv.window;
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int nw = L - nc;
-  const int rec = 2 + D, nrec = a.splits + 1;
+  const int rec = 2 + D, nrec = a.splits + kWindowRecords;
   const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
   float m[kMaxG], l[kMaxG], acc[kMaxG][2 * NP];
 #pragma unroll
@@ -482,7 +485,7 @@ __device__ void window_part(const DecodeArgs& a, float* ws, int s, int hk, int G
 #pragma unroll
     for (int j = 0; j < 2 * NP; ++j) acc[h][j] = 0.f;
   }
-  if (nw > 0) {
+  if (nw > 16 * wi) {
     const uint16_t* kwin = cv.k_window + (size_t(slot) * H + hk) * W * D;
     const uint16_t* vwin = cv.v_window + (size_t(slot) * H + hk) * W * D;
     // query operand: row r16 = 2 h + part
@@ -521,87 +524,99 @@ __device__ void window_part(const DecodeArgs& a, float* ws, int s, int hk, int G
     const float sc1 = a.scale / __shfl(qs, 2 * (h0 + 1) & 15);
     const bool ok0 = g4 < 2 && h0 < G, ok1 = g4 < 2 && h0 + 1 < G;
 
-    uint4 kb[KC];
-    uint32_t vv[16][NP];
-    auto load_block = [&](int t0) {
-      const int rs = (nc + min(t0 + r16, nw - 1)) % W;
-      const uint16_t* kr = kwin + size_t(rs) * D + 8 * g4;
+    // ring of DP blocks in registers: block b lives in slot b % DP and is
+    // requested DP blocks before it is used (each step waits for the oldest
+    // requests only)
+    uint4 kb[DP][KC];
+    uint32_t vv[DP][16][NP];
+    // ring slot of window offset p < nw: (nc + p) mod W without a division
+    // (nc mod W < W and p < W)
+    const int s0 = nc % W;
+    auto ring_row = [&](int p) { const int r = s0 + p; return r >= W ? r - W : r; };
+    auto load_block = [&](int d, int t0) {  // rows past the window repeat its last row
+      const uint16_t* kr = kwin + size_t(ring_row(min(t0 + r16, nw - 1))) * D + 8 * g4;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kb[kc] = *reinterpret_cast<const uint4*>(kr + 32 * kc);
+      for (int kc = 0; kc < KC; ++kc) kb[d][kc] = *reinterpret_cast<const uint4*>(kr + 32 * kc);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const uint32_t* vr = reinterpret_cast<const uint32_t*>(vwin + size_t((nc + min(t0 + u, nw - 1)) % W) * D);
+        const uint32_t* vr = reinterpret_cast<const uint32_t*>(vwin + size_t(ring_row(min(t0 + u, nw - 1))) * D);
 #pragma unroll
-        for (int c = 0; c < NP; ++c) vv[u][c] = vr[64 * c + lane];
+        for (int c = 0; c < NP; ++c) vv[d][u][c] = vr[64 * c + lane];
       }
     };
-    load_block(0);
-    for (int t0 = 0; t0 < nw; t0 += 16) {
-      v4f sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kc], __builtin_bit_cast(v8h, kb[kc]), sacc, 0, 0, 0);
-      uint32_t vcur[16][NP];
+    for (int d = 0; d < DP; ++d) load_block(d, 16 * wi + d * kStep);
+    for (int tb = 16 * wi; tb < nw; tb += DP * kStep) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int d = 0; d < DP; ++d) {
+        const int t0 = tb + d * kStep;
+        if (t0 >= nw) break;
+        v4f sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NP; ++c) vcur[u][c] = vv[u][c];
-      load_block(min(t0 + 16, nw - 1));  // unconditional; the last one repeats rows already read
-      const int t = t0 + r16;
-      const bool tok = t < nw;
-      const float s0 = ok0 && tok ? (sacc[0] + sacc[1]) * sc0 : -INFINITY;
-      const float s1 = ok1 && tok ? (sacc[2] + sacc[3]) * sc1 : -INFINITY;
-      if (a.logits) {
-        if (ok0 && tok) a.logits[(qrow0 + h0) * a.max_ctx + nc + t] = s0;
-        if (ok1 && tok) a.logits[(qrow0 + h0 + 1) * a.max_ctx + nc + t] = s1;
-      }
-      // block maxima per head (rows 0 and 1 hold heads 0, 1 and 2, 3)
-      const float b0 = max16(s0), b1 = max16(s1);
-      const float bm[kMaxG] = {row_value(b0, 0), row_value(b1, 0), row_value(b0, 1), row_value(b1, 1)};
+        for (int kc = 0; kc < KC; ++kc)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kc], __builtin_bit_cast(v8h, kb[d][kc]), sacc, 0, 0, 0);
+        const int t = t0 + r16;
+        const bool tok = t < nw;
+        const float s0 = ok0 && tok ? (sacc[0] + sacc[1]) * sc0 : -INFINITY;
+        const float s1 = ok1 && tok ? (sacc[2] + sacc[3]) * sc1 : -INFINITY;
+        if (a.logits) {
+          if (ok0 && tok) a.logits[(qrow0 + h0) * a.max_ctx + nc + t] = s0;
+          if (ok1 && tok) a.logits[(qrow0 + h0 + 1) * a.max_ctx + nc + t] = s1;
+        }
+        // block maxima per head (rows 0 and 1 hold heads 0, 1 and 2, 3)
+        const float b0 = max16(s0), b1 = max16(s1);
+        const float bm[kMaxG] = {row_value(b0, 0), row_value(b1, 0), row_value(b0, 1), row_value(b1, 1)};
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) {
-        const float mn = fmaxf(m[h], bm[h]);
-        const float r = mn == m[h] ? 1.f : __expf(m[h] - mn);
-        l[h] *= r;
+        for (int h = 0; h < kMaxG; ++h) {
+          const float mn = fmaxf(m[h], bm[h]);
+          const float r = mn == m[h] ? 1.f : __expf(m[h] - mn);
+          l[h] *= r;
 #pragma unroll
-        for (int j = 0; j < 2 * NP; ++j) acc[h][j] *= r;
-        m[h] = mn;
-      }
-      const float m0 = g4 == 0 ? m[0] : m[2], m1 = g4 == 0 ? m[1] : m[3];
-      const float p0 = s0 == -INFINITY ? 0.f : __expf(s0 - m0);
-      const float p1 = s1 == -INFINITY ? 0.f : __expf(s1 - m1);
-      if (g4 < 2) {
-        pbuf[r16 * kMaxG + h0] = p0;
-        pbuf[r16 * kMaxG + h0 + 1] = p1;
-      }
-      const float q0 = sum16(p0), q1 = sum16(p1);
-      l[0] += row_value(q0, 0);
-      l[1] += row_value(q1, 0);
-      l[2] += row_value(q0, 1);
-      l[3] += row_value(q1, 1);
-      lds_fence();
+          for (int j = 0; j < 2 * NP; ++j) acc[h][j] *= r;
+          m[h] = mn;
+        }
+        const float m0 = g4 == 0 ? m[0] : m[2], m1 = g4 == 0 ? m[1] : m[3];
+        const float p0 = s0 == -INFINITY ? 0.f : __expf(s0 - m0);
+        const float p1 = s1 == -INFINITY ? 0.f : __expf(s1 - m1);
+        if (g4 < 2) {
+          pbuf[r16 * kMaxG + h0] = p0;
+          pbuf[r16 * kMaxG + h0 + 1] = p1;
+        }
+        const float q0 = sum16(p0), q1 = sum16(p1);
+        l[0] += row_value(q0, 0);
+        l[1] += row_value(q1, 0);
+        l[2] += row_value(q0, 1);
+        l[3] += row_value(q1, 1);
+        lds_fence();
+        float4 pw[16];  // the block's weights, all requested before the first use
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float4 p = *reinterpret_cast<const float4*>(pbuf + u * kMaxG);
-        const float ph[kMaxG] = {p.x, p.y, p.z, p.w};
+        for (int u = 0; u < 16; ++u) pw[u] = *reinterpret_cast<const float4*>(pbuf + u * kMaxG);
 #pragma unroll
-        for (int c = 0; c < NP; ++c) {
-          const float v0 = f16_bits_to_float(uint16_t(vcur[u][c] & 0xffffu));
-          const float v1 = f16_bits_to_float(uint16_t(vcur[u][c] >> 16));
+        for (int u = 0; u < 16; ++u) {
+          const float4 p = pw[u];
+          const float ph[kMaxG] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-          for (int h = 0; h < kMaxG; ++h) {
-            acc[h][2 * c] = fmaf(ph[h], v0, acc[h][2 * c]);
-            acc[h][2 * c + 1] = fmaf(ph[h], v1, acc[h][2 * c + 1]);
+          for (int c = 0; c < NP; ++c) {
+            const float v0 = f16_bits_to_float(uint16_t(vv[d][u][c] & 0xffffu));
+            const float v1 = f16_bits_to_float(uint16_t(vv[d][u][c] >> 16));
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+              acc[h][2 * c] = fmaf(ph[h], v0, acc[h][2 * c]);
+              acc[h][2 * c + 1] = fmaf(ph[h], v1, acc[h][2 * c + 1]);
+            }
           }
         }
+        lds_fence();
+        // slot d is consumed: request this item's block DP steps ahead
+        // (unconditional; past the window it repeats rows already read)
+        load_block(d, min(t0 + DP * kStep, nw - 1));
       }
-      lds_fence();
     }
   }
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h >= G) break;
-    float* w0 = ws + ((qrow0 + h) * nrec + a.splits) * rec;
+    float* w0 = ws + ((qrow0 + h) * nrec + a.splits + wi) * rec;
     if (lane == 0) {
       w0[0] = m[h];
       w0[1] = l[h];
@@ -744,15 +759,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   if (L > cv.max_pages_per_seq * kPage) L = cv.max_pages_per_seq * kPage;
   if (L > a.max_ctx) L = a.max_ctx;
   const int nc = W > 0 ? max(0, L - W) : L;
-  const int rec = 2 + D, nrec = a.splits + 1;
+  const int rec = 2 + D, nrec = a.splits + kWindowRecords;
   float* ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + part_offset);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(nc, t_begin + a.split_tokens);
-  // the item after the last split attends the recent-token window, exactly,
-  // from the fp16 ring (first wavefront, in the weight operand's LDS), so that
-  // it runs beside the compressed splits instead of after one of them
-  if (split == a.splits) {
-    if (wv == 0) window_part<D>(a, ws, s, hk, G, slot, nc, L, reinterpret_cast<float*>(w_img));
+  // the window_items items after the last split attend the recent-token
+  // window, exactly, from the fp16 ring (first wavefront, in the weight
+  // operand's LDS), so that it runs beside the compressed splits instead of
+  // after one of them
+  if (split >= a.splits) {
+    // ring depth: as many 16-token blocks in flight as the registers allow
+    constexpr int kWinDepth = D == 128 && OCC == 2 ? 2 : 1;
+    if (wv == 0)
+      window_part<D, kWinDepth>(a, ws, s, hk, G, slot, nc, L, split - a.splits, reinterpret_cast<float*>(w_img));
     return;
   }
 
@@ -1239,7 +1258,7 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   const size_t row = size_t(blockIdx.x) * RPB + (RPB > 1 ? wv : 0);  // s * H_q + h
   if (RPB > 1 && row >= size_t(a.num_seqs) * a.num_q_heads) return;  // whole wavefronts; no barrier on this path
   const int s = int(row / a.num_q_heads);
-  const int rec = 2 + D, nrec = a.splits + 1;
+  const int rec = 2 + D, nrec = a.splits + kWindowRecords;
   const float* ws = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.workspace) + part_offset) +
                     row * nrec * rec;
   // compressed splits that hold tokens of this sequence (the rest are empty)
@@ -1250,40 +1269,58 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   L = min(L, min(cv.max_pages_per_seq * kPage, a.max_ctx));
   const int nc = cv.window > 0 ? max(0, L - cv.window) : L;
   const int ns = min(a.splits, (nc + a.split_tokens - 1) / a.split_tokens);
-  auto rec_of = [&](int sp) { return ws + size_t(sp < ns ? sp : a.splits) * rec; };  // the window's record last
+  // records in merge order: the ns compressed splits, then the window's
+  const int NWR = a.window_items;
+  auto rec_of = [&](int sp) { return ws + size_t(sp < ns ? sp : a.splits + (sp - ns)) * rec; };
   // maximum and denominator over the records (every wavefront of the row
-  // alike).  In the wide and the dense forms with fewer than 64 compressed
-  // records, lane sp keeps record sp's weight (lane ns the window's), and the
-  // weights are broadcast from the lanes instead of being read again (every
-  // caller's split index is uniform across its wavefront).
-  const bool in_lanes = (WIDE || ROT == TQ_ROT_DENSE) && ns < 64;
-  float M = -INFINITY, l = 0.f, wl = 0.f;
+  // alike).  In the wide and the dense forms with at most 128 records, lane t
+  // keeps the weights of records t and t + 64, and the weights are broadcast
+  // from the lanes instead of being read again (every caller's record index
+  // is uniform across its wavefront).
+  const bool in_lanes = (WIDE || ROT == TQ_ROT_DENSE) && ns + NWR <= 128;
+  float M = -INFINITY, l = 0.f, wl[2] = {0.f, 0.f};
   if (in_lanes) {
-    float m = -INFINITY, lr = 0.f;
-    if (lane <= ns) {
-      const float* r = rec_of(lane);
-      m = r[0];
-      lr = r[1];
-    }
-    M = wave_max(m);
-    wl = m == -INFINITY ? 0.f : __expf(m - M);
-    l = wave_sum(wl * lr);
+    // lane t holds records t and t + 64
+    float m[2] = {-INFINITY, -INFINITY}, lr[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < ns + NWR) {
+        const float* r = rec_of(lane + 64 * i);
+        m[i] = r[0];
+        lr[i] = r[1];
+      }
+    M = wave_max(fmaxf(m[0], m[1]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wl[i] = m[i] == -INFINITY ? 0.f : __expf(m[i] - M);
+    l = wave_sum(fmaf(wl[0], lr[0], wl[1] * lr[1]));
   } else {
-    for (int sp = lane; sp <= ns; sp += 64) M = fmaxf(M, rec_of(sp)[0]);
+    for (int sp = lane; sp < ns + NWR; sp += 64) M = fmaxf(M, rec_of(sp)[0]);
     M = wave_max(M);
-    for (int sp = lane; sp <= ns; sp += 64) {
+    for (int sp = lane; sp < ns + NWR; sp += 64) {
       const float m = rec_of(sp)[0];
       if (m != -INFINITY) l = fmaf(__expf(m - M), rec_of(sp)[1], l);
     }
     l = wave_sum(l);
   }
-  // weight of compressed split sp < ns, or of the window's record (sp = splits)
+  // weight of record sp in merge order (compressed splits below ns); sp is
+  // uniform across the calling wavefront
   auto weight = [&](int sp) {
-    if (in_lanes) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sp < ns ? sp : ns));
-    const float m = ws[size_t(sp) * rec];
+    if (in_lanes)
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp < 64 ? wl[0] : wl[1]), sp & 63));
+    const float m = rec_of(sp)[0];
     return m == -INFINITY ? 0.f : __expf(m - M);
   };
-  const float fw = weight(a.splits);
+  float fw[kWindowRecords];
+#pragma unroll
+  for (int j = 0; j < kWindowRecords; ++j) fw[j] = j < NWR ? weight(ns + j) : 0.f;
+  // the window records' weighted value sum at coordinate c
+  auto window_sum = [&](int c) {
+    float aw = 0.f;
+#pragma unroll
+    for (int j = 0; j < kWindowRecords; ++j)
+      if (fw[j] != 0.f) aw = fmaf(fw[j], rec_of(ns + j)[2 + c], aw);
+    return aw;
+  };
   if constexpr (ROT == TQ_ROT_FWHT) {
     // compressed value sums, coordinates r * 64 + lane
     float ar[R];
@@ -1337,7 +1374,7 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
     for (int r = 0; r < R; ++r) {
       const int c = r * 64 + lane;
       const float o = apply_sign(ar[r] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c));
-      const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
+      const float aw = window_sum(c);
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
   } else {
@@ -1387,7 +1424,7 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
       float o = 0.f;
 #pragma unroll
       for (int q = 0; q < KQ; ++q) o += buf[q * D + c];
-      const float aw = fw != 0.f ? fw * ws[size_t(a.splits) * rec + 2 + c] : 0.f;
+      const float aw = window_sum(c);
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
   }
@@ -1403,8 +1440,8 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
                      0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one work item per (sequence, kv head, split), plus one per (sequence, kv head) for the window
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits + 1),
+  // one work item per (sequence, kv head, split), plus window_items per (sequence, kv head) for the window
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits + a.window_items),
                      dim3(64 * NW), 0, st, a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -243,7 +243,11 @@ SplitPlan plan_splits(const tq_config& cfg, int num_seqs, int max_ctx) {
   if (split_tokens < tile) split_tokens = tile;
   splits = (ctx + split_tokens - 1) / split_tokens;
   if (splits < 1) splits = 1;
-  return {int(splits), int(split_tokens)};
+  // The window's items run after the compressed ones: kWindowRecords short
+  // ones per (sequence, KV head) where they fit in the slots the compressed
+  // items leave, else one (the compressed items already fill the GPU).
+  const int window_items = units * kWindowRecords <= items ? kWindowRecords : 1;
+  return {int(splits), int(split_tokens), window_items};
 }
 
 Codec make_codec(const tq_config& c) {

@@ -132,6 +132,10 @@ struct AppendArgs {
   int32_t parts;  // workers per (sequence, kv head), set by launch_append
 };
 
+// Decode partial records per (sequence, query head) beyond the splits': one
+// per work item of the recent-token window.
+constexpr int kWindowRecords = 4;
+
 struct DecodeArgs {
   CacheView cache;
   const uint8_t* params;
@@ -140,10 +144,11 @@ struct DecodeArgs {
   const int32_t* ctx_len;
   float* out;
   float* workspace;   // plain path: [num_seqs][H_q][splits][2 + 2d]; matrix-core path: query
-                      // operands (decode_prep_bytes), then [num_seqs][H_q][splits][2 + d]
+                      // operands (decode_prep_bytes), then [num_seqs][H_q][splits + kWindowRecords][2 + d]
   float* logits;      // optional [num_seqs][H_q][max_ctx]
   int32_t num_seqs, num_q_heads, q_dtype, key_mse_bits, value_bits;
   int32_t splits, split_tokens, max_ctx;
+  int32_t window_items;  // matrix-core path: 1 .. kWindowRecords
   float scale;
 };
 
@@ -159,6 +164,7 @@ struct DequantArgs {
 struct SplitPlan {
   int splits;
   int split_tokens;
+  int window_items;  // matrix-core path: work items of the recent-token window per (sequence, KV head)
 };
 // At most kMaxSplits context splits per (sequence, KV head).
 constexpr int kMaxSplits = 2048;
