@@ -607,7 +607,8 @@ def main(argv=None):
                           "achieved_GBs": round(oc["bytes"] / (oc["ms"] / 1e3) / 1e9, 2)},
         "library_build_id": tqa.build_id(),
     }
-    if w.name in QUALITY_HEAD:
+    # (not in counter runs: its logit dump would be counted as the last decode's traffic)
+    if w.name in QUALITY_HEAD and not args.calibrate_copy:
         line["quality_vs_exact"] = quality_vs_exact(w, r["setup"])
     del r
     if not args.no_extra:
