@@ -661,19 +661,22 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // Two wavefronts per SIMD leave 256.
 constexpr int kRegBudget = 256;
 constexpr int kRegMargin = 68;
-// (EXT adds two sidecar words per scored page, the lanes' word offsets and
-// the format's runtime fields.)
+// fmt: 0 the default format, 1 an extended one (EXT adds two sidecar words per
+// scored page, the lanes' word offsets and the format's runtime fields), 2
+// group-quantized values (GV adds each scored page's scale and zero words, kept
+// twice, a tile's value words instead of a pair's, and the group sums).
 constexpr int kExtMargin = 40;
-__host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds, bool ext = false) {
+__host__ __device__ constexpr int split_regs(int D, int MK, int BV, int NW, bool q_in_lds, int fmt = 0) {
   return num_planes(BV) * (D / 16 / NW) * 4 + (q_in_lds ? 0 : (num_planes(MK) + 1) * (D / 128) * 8) +
          (8 / NW) * ((MK + 1) * (D / 128) + 3) + (D / 16 / NW) * BV + num_planes(MK) * (D / 128) * 4 + kRegMargin +
-         (ext ? 2 * (8 / NW) + kExtMargin + (MK == 4 ? kExtMargin : 0) : 0);
+         (fmt ? 2 * (8 / NW) + kExtMargin + (MK == 4 ? kExtMargin : 0) : 0) +
+         (fmt == 2 ? 2 * (8 / NW) * (D / 32) + (D / 16 / NW) * BV + 2 * (D / 32) : 0);
 }
 __host__ __device__ constexpr bool split_shape_ok(int D, int NW) {
   return (D / 16) % NW == 0 && 8 % NW == 0 && ((D / 16) / NW) % 2 == 0;
 }
-__host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds, bool ext = false) {
-  return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds, ext) <= kRegBudget;
+__host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, bool q_in_lds, int fmt = 0) {
+  return split_shape_ok(D, NW) && split_regs(D, MK, BV, NW, q_in_lds, fmt) <= kRegBudget;
 }
 // Wavefronts resident per SIMD.  With three or four value bits at d = 128 the
 // work of a block divides over four wavefronts that each fit in 168 registers
@@ -682,23 +685,23 @@ __host__ __device__ constexpr bool split_fits(int D, int MK, int BV, int NW, boo
 // SIMD: at d = 128 with at most two value bits one wavefront per work item
 // measured faster than four at four per SIMD, whose recent-token window then
 // runs on one of the four.
-__host__ __device__ constexpr int split_occupancy(int D, int MK, int BV, bool ext = false) {
-  return D == 128 && BV > 2 && !ext ? 3 : 2;
+__host__ __device__ constexpr int split_occupancy(int D, int MK, int BV, int fmt = 0) {
+  return D == 128 && BV > 2 && !fmt ? 3 : 2;
 }
 // Variants where the estimate above is too optimistic (the compiled loop
 // spills at the estimated count) and the wavefront count that compiles clean.
-__host__ __device__ constexpr int split_waves_override(int D, int MK, int BV, bool ext = false) {
-  return split_occupancy(D, MK, BV, ext) > 2 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
+__host__ __device__ constexpr int split_waves_override(int D, int MK, int BV, int fmt = 0) {
+  return split_occupancy(D, MK, BV, fmt) > 2 ? 4 : D == 256 && MK == 1 && BV == 3 ? 4 : D == 256 && MK == 2 && BV == 4 ? 8 : 0;
 }
 // wavefronts per work item: the fewest whose registers fit two wavefronts per SIMD
-__host__ __device__ constexpr int split_waves(int D, int MK, int BV, bool ext = false) {
-  return split_waves_override(D, MK, BV, ext) ? split_waves_override(D, MK, BV, ext)
-       : split_fits(D, MK, BV, 1, true, ext) ? 1 : split_fits(D, MK, BV, 2, true, ext) ? 2
-       : split_fits(D, MK, BV, 4, true, ext) || !split_shape_ok(D, 8) ? 4 : 8;
+__host__ __device__ constexpr int split_waves(int D, int MK, int BV, int fmt = 0) {
+  return split_waves_override(D, MK, BV, fmt) ? split_waves_override(D, MK, BV, fmt)
+       : split_fits(D, MK, BV, 1, true, fmt) ? 1 : split_fits(D, MK, BV, 2, true, fmt) ? 2
+       : split_fits(D, MK, BV, 4, true, fmt) || !split_shape_ok(D, 8) ? 4 : 8;
 }
 // query operands stay in registers when they fit, else each MFMA reads them from LDS
-__host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV, bool ext = false) {
-  return split_occupancy(D, MK, BV, ext) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV, ext), false, ext);
+__host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV, int fmt = 0) {
+  return split_occupancy(D, MK, BV, fmt) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV, fmt), false, fmt);
 }
 
 // Re-base a head's reference maximum only when a block's maximum exceeds it by
@@ -713,16 +716,27 @@ constexpr float kLn2 = 0.6931471805599453f;
 // store (their plane coefficients are zero), the QJL plane is each group's
 // last, scale-corrected keys skip it, and sidecar records are staged in LDS
 // and added to the scores.
-template <int D, int MK, int BV, int NW, bool QL, int OCC, bool EXT>
+//
+// GV (group-quantized values, with EXT): a value tile's 16 operand rows are 16
+// consecutive coordinates, so that a tile lies in one 32-coordinate group and
+// takes that group's weight operand p_t scale_{t,g}; codes are linear in their
+// bits, so only the single-bit planes are multiplied:
+//   sum_t p_t v_{t,c} = sum_t p_t zero_{t,g} + (2^b - 1)/2 sum_t p_t scale_{t,g}
+//                       - sum_j 2^(j-1) sum_t p_t scale_{t,g} s_{j,t,c},  s = 1 - 2 bit,
+// the first two sums kept per (head, group) in registers; the result stays in
+// the value's own basis (no inverse rotation in the merge).
+template <int D, int MK, int BV, int NW, bool QL, int OCC, bool EXT, bool GV = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
+  static_assert(!GV || EXT, "group-quantized values are an extended format");
   constexpr int KP = num_planes(MK);   // key plane products
-  constexpr int VP = num_planes(BV);   // value plane products
+  constexpr int VP = GV ? BV : num_planes(BV);  // value plane products (GV: single planes)
   constexpr int KH = D / 128;          // 128-coordinate halves of the score contraction
   constexpr int NCB = D / 16;          // 16-coordinate blocks of the value contraction
   constexpr int CBW = NCB / NW;        // coordinate blocks per wavefront
   constexpr int PPW = 8 / NW;          // pages scored per wavefront per block
   constexpr int KW = (MK + 1) * KH;    // key words per lane per page
-  constexpr int VW = (CBW / 2) * BV;   // value words per lane per page pair
+  constexpr int VW = (GV ? CBW : CBW / 2) * BV;  // value words per lane per page pair
+  constexpr int NG = D / kGroup;       // GV: scale / zero groups per token
   // scheduling fences between page pairs of the scores, only where the extra
   // pages in flight would spill (d = 256, 3 key MSE bits, 2 value bits);
   // elsewhere the compiler interleaves more pages across the chained MFMAs
@@ -731,7 +745,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   constexpr bool kRollKeys = !kPlaneOuter;  // key pages re-requested one by one
   static_assert(NCB % NW == 0 && 8 % NW == 0 && CBW % 2 == 0, "wavefront split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t w_img[2048];                       // softmax-weight operand
+  __shared__ __attribute__((aligned(16))) uint8_t w_img[GV ? NG * 2048 : 2048];   // softmax-weight operand(s)
+  __shared__ float gsum[GV ? NW * kMaxG * NG * 2 : 1];  // GV: per-wavefront zero and scale sums
   __shared__ __attribute__((aligned(16))) uint8_t q_img[QL ? (KP + 1) * KH * 2048 : 16];  // query operands
   __shared__ float red[NW][8];
   __shared__ float fin[NW][kMaxG];
@@ -836,6 +851,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   uint32_t v_pair = 0;      // EXT: bytes between the lane's consecutive value pairs
   int q_word = MK;          // EXT: the lane's QJL word among its group's words
   uint32_t side_off = 0;    // EXT: this lane's word of its token's sidecar record
+  uint32_t gv_off[GV ? CBW : 1];  // GV: the words of this lane's coordinate pair in each of its tiles
   if constexpr (EXT) {
     const int kh = g4 >= 2 ? 1 : 0;  // score lane groups 2-3 hold upper-half coordinates
     const int vh = r16 >= 8 ? 1 : 0;  // value rows 8-15 likewise
@@ -847,6 +863,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     v_pair = uint32_t(cd.vbits[vh] * 4);
     q_word = cd.kbits[kh];
     side_off = uint32_t(cd.key_side_off + r16 * cd.side_bytes + 4 * g4);
+    if constexpr (GV) {
+      // tile CBW wv + c holds coordinates 16 (CBW wv + c) + row; the lane's row is r16
+#pragma unroll
+      for (int c = 0; c < CBW; ++c)
+        gv_off[c] = uint32_t(value_pair_word(cd, (16 * (CBW * wvu + c) + r16) / 2, D) * 4);
+      vn_off = uint32_t(cd.value_tail_off + r16 * NG * 4);  // the token's (scale, zero) pairs
+    }
   }
   typedef const int __attribute__((address_space(4))) const_int;
   const const_int* bt = (const const_int*)(cv.block_table + size_t(slot) * cv.max_pages_per_seq);
@@ -890,12 +913,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   float m_ref = -1e30f;     // reference maximum of head g4 (score layout, base-2 logits); finite so
                             // that exp2(-inf - m_ref) = 0
   float l_part = 0.f;       // this lane's share of head g4's denominator, relative to m_ref
+  // GV: this lane's shares of sum_t p_t zero_{t,g} and sum_t p_t scale_{t,g} for head g4
+  float zacc[GV ? NG : 1], sacc[GV ? NG : 1];
+#pragma unroll
+  for (int g = 0; g < (GV ? NG : 1); ++g) zacc[g] = sacc[g] = 0.f;
 
   int kid[PPW];  // page ids of the scored pages of the block being loaded
   uint32_t kw[PPW][KW];
   float2 kn[PPW];
   float vn[PPW];
   uint32_t sw[EXT ? PPW : 1][2];  // EXT: sidecar words g4 and g4 + 4 of the lane's token record
+  uint32_t gsz[GV ? PPW : 1][GV ? NG : 1];  // GV: the lane's token's (fp16 scale, fp16 zero) per group
   uint32_t vw[2][VW];  // value words of the block
   auto load_key_page = [&](int j) {
     kid[j] = checked(nkid[j]);
@@ -919,7 +947,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       load_words<KW>(kb + ko, kw[j]);
     }
     kn[j] = *reinterpret_cast<const float2*>(kb + kno);
-    vn[j] = *reinterpret_cast<const float*>(vb + vno);
+    if constexpr (GV) load_words<NG>(vb + vno, gsz[j]);
+    else vn[j] = *reinterpret_cast<const float*>(vb + vno);
   };
   // The lane's QJL word among the words of its group (EXT: after the
   // half's own planes), selected with per-lane masks (a select on the word's
@@ -972,7 +1001,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       mine = g4 == 1 ? p1 : mine;
       mine = g4 == 2 ? p2 : mine;
       mine = g4 == 3 ? p3 : mine;
-      if constexpr (EXT) {
+      if constexpr (GV) {
+        const uint8_t* vb = vbase + size_t(mine) * vstride;
+#pragma unroll
+        for (int c = 0; c < CBW; ++c) load_words_a4<BV>(vb + gv_off[c], vw[hp] + c * BV);
+      } else if constexpr (EXT) {
         const uint8_t* vb = vbase + size_t(mine) * vstride + v_off;
 #pragma unroll
         for (int cp = 0; cp < CBW / 2; ++cp) load_words_a4<BV>(vb + cp * v_pair, vw[hp] + cp * BV);
@@ -999,6 +1032,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     fetch_ids(tb + kBlock);  // the next block's pages; their waits fall after the scores
     // ---------------------------------------------- scores of this wavefront's pages
     float sc[PPW], vnu[PPW];
+    uint32_t gcur[GV ? PPW : 1][GV ? NG : 1];  // GV: this block's (scale, zero) pairs, kept past the reload
     bool kok[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) kok[j] = kid[j] >= 0;
@@ -1044,7 +1078,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       float2 knj = kn[j];
-      float vnj = vn[j];
+      float vnj;
+      if constexpr (GV) {  // the token's largest group scale bounds its weights
+        vnj = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          gcur[j][g] = gsz[j][g];
+          vnj = fmaxf(vnj, f16_bits_to_float(uint16_t(gsz[j][g] & 0xffffu)));
+        }
+      } else {
+        vnj = vn[j];
+      }
       if constexpr (!kPlaneOuter) {
 #pragma unroll
         for (int hf = 0; hf < KH; ++hf) {
@@ -1108,6 +1152,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       const float m_new = rebase ? blk_max : m_ref;
       const float r = m_new == m_ref ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       l_part *= r;
+#pragma unroll
+      for (int g = 0; g < (GV ? NG : 1); ++g) {
+        zacc[g] *= r;
+        sacc[g] *= r;
+      }
       // value layout: column r16 = (head r16 / 4, part r16 % 4)
       const float rv = row_value(r, r16 >> 2);
 #pragma unroll
@@ -1135,24 +1184,59 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       const float p0 = __builtin_amdgcn_exp2f(sc[j] - m_ref);  // 0 for sc = -inf
       const float p1 = j + 1 < PPW ? __builtin_amdgcn_exp2f(sc[j + 1] - m_ref) : 0.f;
       l_part += p0 + p1;
-      uint32_t lo, hi;
-      fp8_split4_pair(p0 * vnu[j] * wscale, j + 1 < PPW ? p1 * vnu[j + 1] * wscale : 0.f,
-                      __builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), lo, hi);
+      // weight image g holds p_t scale_{t,g} (GV); the single image p_t nu_t otherwise
 #pragma unroll
-      for (int u = 0; u < 2 && j + u < PPW; ++u) {
-        const int t = (wvu * PPW + j + u) * kPage + r16;
-        uint8_t* o = w_img + fp8_image_offset(g4 * 4, 32 * (t / 32) + fp4_bit_elem(t % 32));
-        uint32_t l8 = lo >> (8 * u), h8 = hi >> (8 * u);
-        if (u) asm volatile("" : "+v"(l8), "+v"(h8));  // keeps the >> 16 below a byte-2 store
-        o[0] = uint8_t(l8);
-        o[16] = uint8_t(l8 >> 16);
-        o[32] = uint8_t(h8);
-        o[48] = uint8_t(h8 >> 16);
+      for (int g = 0; g < (GV ? NG : 1); ++g) {
+        float x0, x1;
+        if constexpr (GV) {
+          const float s0 = f16_bits_to_float(uint16_t(gcur[j][g] & 0xffffu));
+          const float z0 = f16_bits_to_float(uint16_t(gcur[j][g] >> 16));
+          const float s1 = j + 1 < PPW ? f16_bits_to_float(uint16_t(gcur[j + 1][g] & 0xffffu)) : 0.f;
+          const float z1 = j + 1 < PPW ? f16_bits_to_float(uint16_t(gcur[j + 1][g] >> 16)) : 0.f;
+          zacc[g] = fmaf(p0, z0, fmaf(p1, z1, zacc[g]));
+          sacc[g] = fmaf(p0, s0, fmaf(p1, s1, sacc[g]));
+          x0 = p0 * s0 * wscale;
+          x1 = p1 * s1 * wscale;
+        } else {
+          x0 = p0 * vnu[j] * wscale;
+          x1 = j + 1 < PPW ? p1 * vnu[j + 1] * wscale : 0.f;
+        }
+        uint32_t lo, hi;
+        fp8_split4_pair(x0, x1, __builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), lo, hi);
+#pragma unroll
+        for (int u = 0; u < 2 && j + u < PPW; ++u) {
+          const int t = (wvu * PPW + j + u) * kPage + r16;
+          uint8_t* o = w_img + g * 2048 + fp8_image_offset(g4 * 4, 32 * (t / 32) + fp4_bit_elem(t % 32));
+          uint32_t l8 = lo >> (8 * u), h8 = hi >> (8 * u);
+          if (u) asm volatile("" : "+v"(l8), "+v"(h8));  // keeps the >> 16 below a byte-2 store
+          o[0] = uint8_t(l8);
+          o[16] = uint8_t(l8 >> 16);
+          o[32] = uint8_t(h8);
+          o[48] = uint8_t(h8 >> 16);
+        }
       }
     }
     block_sync<NW>();
     // ---------------------------------------------- value tiles of this wavefront
-    {
+    if constexpr (GV) {
+      // operand row r16 of tile CBW wv + c is coordinate 16 (CBW wv + c) + r16: its
+      // bits are the low (even r16) or high half of its pair's words
+      const uint32_t sel = (r16 & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int c = 0; c < CBW; c += 2) {
+        const uint8_t* wi = w_img + ((CBW * wvu + c) / 2) * 2048;  // the tiles' group
+        const uint4 lo = reinterpret_cast<const uint4*>(wi)[lane];
+        const uint4 hi = reinterpret_cast<const uint4*>(wi + 1024)[lane];
+        const v8i wop = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int b = 0; b < BV; ++b) {
+            const uint32_t w = __builtin_amdgcn_perm(vw[1][(c + u) * BV + b], vw[0][(c + u) * BV + b], sel);
+            acc[b][c + u] = mfma_f4_f8(fp4_operand(bits_to_fp4_pm6_dwords(w)), wop, acc[b][c + u], scale_b);
+          }
+      }
+    } else {
       const uint4 lo = reinterpret_cast<const uint4*>(w_img)[lane];
       const uint4 hi = reinterpret_cast<const uint4*>(w_img + 1024)[lane];
       const v8i wop = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
@@ -1208,11 +1292,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   const int ch = r16 >> 2, cq = r16 & 3;
   const float part_w = cq == 0 ? 1.f : cq == 1 ? 0.0625f : cq == 2 ? 0.00390625f : 0.000244140625f;
   float* wsh = ws + ((size_t(s) * a.num_q_heads + hk * G + ch) * nrec + split) * rec + 2;
+  if constexpr (GV) {
+    // the per-(head, group) sums of this wavefront's tokens, to LDS
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float zs = sum16(zacc[g]), ss = sum16(sacc[g]);
+      if (r16 == 0) {
+        gsum[((wv * kMaxG + g4) * NG + g) * 2] = zs;
+        gsum[((wv * kMaxG + g4) * NG + g) * 2 + 1] = ss;
+      }
+    }
+    block_sync<NW>();  // (one wavefront reads its own LDS writes in order)
+  }
   float cvals[VP];
+  if constexpr (!GV) {
 #pragma unroll
-  for (int p = 0; p < VP; ++p) cvals[p] = coef_v[odd_subset(BV, p)] * (1.f / kPm6);  // planes read +-6
+    for (int p = 0; p < VP; ++p) cvals[p] = coef_v[odd_subset(BV, p)] * (1.f / kPm6);  // planes read +-6
+  }
 #pragma unroll
-  for (int c = 0; c < CBW; ++c)
+  for (int c = 0; c < CBW; ++c) {
+    float half_const = 0.f;  // GV: (2^b - 1) / 2 for the tile's half
+    if constexpr (GV) {
+      // plane j carries -2^(j-1) s_j, read as +-6
+      const int bits = cd.vbits[16 * (CBW * wv + c) >= D / 2 ? 1 : 0];
+#pragma unroll
+      for (int p = 0; p < VP; ++p) cvals[p] = p < bits ? -float(1 << p) / (2.f * kPm6) : 0.f;
+      half_const = 0.5f * float((1 << bits) - 1);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = 0.f;
@@ -1221,9 +1327,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
       v *= part_w;
       v += dpp<0xB1>(v);
       v += dpp<0x4E>(v);
-      const int coord = NCB * (4 * g4 + i) + CBW * wv + c;
-      if (cq == 0 && ch < G) wsh[coord] = v;
+      const int coord = GV ? 16 * (CBW * wv + c) + 4 * g4 + i : NCB * (4 * g4 + i) + CBW * wv + c;
+      if (cq == 0 && ch < G) {
+        if constexpr (GV) {
+          const int g = coord / kGroup;
+          float zs = 0.f, ss = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) {
+            zs += gsum[((w2 * kMaxG + ch) * NG + g) * 2];
+            ss += gsum[((w2 * kMaxG + ch) * NG + g) * 2 + 1];
+          }
+          v += fmaf(half_const, ss, zs);
+        }
+        wsh[coord] = v;
+      }
     }
+  }
 }
 
 // Merge the compressed splits of one (sequence, query head) by log-sum-exp,
@@ -1263,6 +1382,8 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
                     row * nrec * rec;
   // compressed splits that hold tokens of this sequence (the rest are empty)
   const CacheView& cv = a.cache;
+  // group-quantized values are accumulated in their own basis: no inverse rotation
+  const bool rotated = cv.codec.value_mode != TQ_VALUE_GROUP;
   const int slot = a.seq_slots[s];
   int L = a.ctx_len[s];
   if (slot < 0 || slot >= cv.max_seqs || L < 0) L = 0;
@@ -1369,11 +1490,11 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
         ar[r] = (buf[c] + buf[D + c]) + (buf[2 * D + c] + buf[3 * D + c]);
       }
     }
-    wave_fwht<R>(ar, lane);
+    if (rotated) wave_fwht<R>(ar, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int c = r * 64 + lane;
-      const float o = apply_sign(ar[r] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c));
+      const float o = rotated ? apply_sign(ar[r] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c)) : ar[r];
       const float aw = window_sum(c);
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
@@ -1387,8 +1508,10 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
     // loads overlap the merge's
     const float* piv = reinterpret_cast<const float*>(a.params + kOffDense) + size_t(2) * D * D + size_t(k * J) * D + c;
     float pv[J];
+    if (rotated) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) pv[j] = piv[size_t(j) * D];
+      for (int j = 0; j < J; ++j) pv[j] = piv[size_t(j) * D];
+    }
     float ar = 0.f;
     {
       int sp = k;
@@ -1415,8 +1538,12 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
     __syncthreads();
     const float* sum = buf + KQ * D + k * J;
     float o4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rotated) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) o4[j % 4] = fmaf(pv[j], sum[j], o4[j % 4]);
+      for (int j = 0; j < J; ++j) o4[j % 4] = fmaf(pv[j], sum[j], o4[j % 4]);
+    } else if (k == 0) {
+      o4[0] = buf[KQ * D + c];
+    }
     __syncthreads();  // every read of the slices above is done
     buf[k * D + c] = (o4[0] + o4[1]) + (o4[2] + o4[3]);
     __syncthreads();
@@ -1430,18 +1557,19 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   }
 }
 
-template <int D, int MK, int BV, int ROT, bool EXT>
+template <int D, int MK, int BV, int ROT, bool EXT, bool GV>
 hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) {
-  constexpr int NW = split_waves(D, MK, BV, EXT);
-  constexpr bool QL = split_q_in_lds(D, MK, BV, EXT);
-  constexpr int OCC = split_occupancy(D, MK, BV, EXT);
+  constexpr int FMT = GV ? 2 : EXT ? 1 : 0;
+  constexpr int NW = split_waves(D, MK, BV, FMT);
+  constexpr bool QL = split_q_in_lds(D, MK, BV, FMT);
+  constexpr int OCC = split_occupancy(D, MK, BV, FMT);
   const int H = a.cache.num_kv_heads;
   hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(ROT == TQ_ROT_DENSE ? 1024 : 256),
                      0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // one work item per (sequence, kv head, split), plus window_items per (sequence, kv head) for the window
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT>), dim3(a.num_seqs * H, a.splits + a.window_items),
+  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT, GV>), dim3(a.num_seqs * H, a.splits + a.window_items),
                      dim3(64 * NW), 0, st, a, part_offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1467,10 +1595,10 @@ Bits kernel_bits(const tq_config& cfg) {
   return {k.kbits[0] > k.kbits[1] ? k.kbits[0] : k.kbits[1], k.vbits[0] > k.vbits[1] ? k.vbits[0] : k.vbits[1]};
 }
 
-template <int D, int ROT, bool EXT>
+template <int D, int ROT, bool EXT, bool GV>
 hipError_t dispatch_bits(const DecodeArgs& a, Bits b, size_t part_offset, hipStream_t st) {
 #define TQ_CASE(MK_, BV_) \
-  if (b.mk == MK_ && b.bv == BV_) return launch_mfma<D, MK_, BV_, ROT, EXT>(a, part_offset, st);
+  if (b.mk == MK_ && b.bv == BV_) return launch_mfma<D, MK_, BV_, ROT, EXT, GV>(a, part_offset, st);
   TQ_CASE(1, 1) TQ_CASE(1, 2) TQ_CASE(1, 3) TQ_CASE(1, 4)
   TQ_CASE(2, 1) TQ_CASE(2, 2) TQ_CASE(2, 3) TQ_CASE(2, 4)
   TQ_CASE(3, 1) TQ_CASE(3, 2) TQ_CASE(3, 3) TQ_CASE(3, 4)
@@ -1488,8 +1616,8 @@ int decode_mfma_items(const tq_config& cfg) {
   const int d = cfg.head_dim;
   if (b.mk < 1 || b.mk > 4 || b.bv < 1 || b.bv > 4 || (d != 128 && d != 256)) return 2048;
   // work items that fill every SIMD once: 1024 SIMDs x resident wavefronts / wavefronts per item
-  const bool ext = make_codec(cfg).ext != 0;
-  return 1024 * split_occupancy(d, b.mk, b.bv, ext) / split_waves(d, b.mk, b.bv, ext);
+  const int fmt = cfg.value_mode == TQ_VALUE_GROUP ? 2 : make_codec(cfg).ext ? 1 : 0;
+  return 1024 * split_occupancy(d, b.mk, b.bv, fmt) / split_waves(d, b.mk, b.bv, fmt);
 }
 
 size_t decode_prep_bytes(const tq_config& cfg, int num_seqs) {
@@ -1502,25 +1630,27 @@ size_t decode_prep_bytes(const tq_config& cfg, int num_seqs) {
 }
 
 // The matrix-core path takes head_dim 128 and 256, GQA groups up to 4, and
-// every stored format whose values are Lloyd-Max coded (group-quantized
-// values take the plain kernel).
+// every stored format.
 bool decode_mfma_supported(const tq_config& cfg) {
   return (cfg.head_dim == 128 || cfg.head_dim == 256) && cfg.num_q_heads / cfg.num_kv_heads <= kMaxG &&
-         cfg.page_tokens == kPage && cfg.window <= 1024 && cfg.value_mode == TQ_VALUE_LLOYD;
+         cfg.page_tokens == kPage && cfg.window <= 1024;
 }
 
 int launch_decode_mfma(const tq_config& cfg, const DecodeArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool dense = cfg.rotation == TQ_ROT_DENSE;
   const bool ext = make_codec(cfg).ext != 0;
+  const bool gv = cfg.value_mode == TQ_VALUE_GROUP;
   const Bits b = kernel_bits(cfg);
   const size_t part_offset = decode_prep_bytes(cfg, a.num_seqs);
 #define TQ_DISPATCH(D_)                                                                                   \
   if (cfg.head_dim == D_) {                                                                               \
-    if (ext) return dense ? dispatch_bits<D_, TQ_ROT_DENSE, true>(a, b, part_offset, st)                  \
-                          : dispatch_bits<D_, TQ_ROT_FWHT, true>(a, b, part_offset, st);                  \
-    return dense ? dispatch_bits<D_, TQ_ROT_DENSE, false>(a, b, part_offset, st)                          \
-                 : dispatch_bits<D_, TQ_ROT_FWHT, false>(a, b, part_offset, st);                          \
+    if (gv) return dense ? dispatch_bits<D_, TQ_ROT_DENSE, true, true>(a, b, part_offset, st)             \
+                         : dispatch_bits<D_, TQ_ROT_FWHT, true, true>(a, b, part_offset, st);             \
+    if (ext) return dense ? dispatch_bits<D_, TQ_ROT_DENSE, true, false>(a, b, part_offset, st)           \
+                          : dispatch_bits<D_, TQ_ROT_FWHT, true, false>(a, b, part_offset, st);           \
+    return dense ? dispatch_bits<D_, TQ_ROT_DENSE, false, false>(a, b, part_offset, st)                   \
+                 : dispatch_bits<D_, TQ_ROT_FWHT, false, false>(a, b, part_offset, st);                   \
   }
   TQ_DISPATCH(128) TQ_DISPATCH(256)
 #undef TQ_DISPATCH
