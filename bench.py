@@ -339,36 +339,34 @@ def run_gpu(w, steps, warmup, copies, keep_head=None):
         tqa.decode_attention(S.cfg, S.params, S.caches[i % copies], S.q, S.dec_slots, S.dec_lens, S.max_ctx, S.out,
                              S.ws, stream=stream)
 
-    def timed(body, n, first):
-        """Stream time of n back-to-back iterations of body(first + i), with
-        events only around the whole run (an event between two calls leaves
-        the GPU idle while it is processed)."""
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for i in range(n):
-            body(first + i)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
-
     for i in range(warmup):
         append(i)
         decode(i)
     torch.cuda.synchronize()
-    # the step: append then decode, steps times
+    # the step, steps times: append then decode, each call between a pair of
+    # events on its stream (their durations are the calls' launch durations;
+    # the pair around the loop times the steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    total_ms = timed(lambda i: (append(i), decode(i)), steps, warmup)
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        append(warmup + i)
+        ev[i][1].record(stream)
+        decode(warmup + i)
+        ev[i][2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    # each call alone, back to back on the same rotation of cache copies: its
-    # average duration on the stream
-    app_ms = timed(append, steps, warmup) / steps
-    dec_ms = timed(decode, steps, warmup) / steps
+    total_ms = t0.elapsed_time(t1)
+    app_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     if not torch.isfinite(S.out).all():
         raise RuntimeError("non-finite decode output")
     log(f"{steps} steps: {total_ms:.3f} ms on the stream ({wall * 1e3:.1f} ms wall); "
-        f"append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us per call (each call timed back to back)")
+        f"append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us per call")
     return dict(total_ms=total_ms, app_ms=app_ms, dec_ms=dec_ms, lens=S.lens, app_counts=S.app_counts,
                 app_lens_after=S.app_lens_after, copies=copies, setup=S)
 
