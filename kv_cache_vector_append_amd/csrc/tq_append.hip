@@ -16,15 +16,16 @@
 //    comment above it.
 //  * append_dense_kernel (dense rotation, d = 128 or 256): GEMMs of 64-token
 //    tiles on the matrix cores; see the comment above it.
-//  * append_kernel (d = 256 FWHT, dense d = 64, and short appends): one
-//    64-lane wavefront per (sequence, kv head, part); the part strides over the
-//    pages the sequence's new tokens touch, so a page is only ever written by
-//    one wavefront in a call.  Lanes hold coordinates (lane l owns coordinates
-//    r*64 + l), so the Walsh-Hadamard butterflies are cross-lane shuffles, the
-//    norms are wavefront reductions, and each key bit-plane row is one
-//    wavefront ballot.  Value bit-planes are stored per coordinate (16 token
-//    bits), which each lane accumulates in registers over the page's tokens and
-//    writes once.
+//  * append_kernel (d = 256 FWHT, dense d = 64, and short appends): two
+//    64-lane wavefronts per (sequence, kv head, part), one for the keys and
+//    one for the values; the part strides over the pages the sequence's new
+//    tokens touch, so a page is only ever written by one workgroup in a call.
+//    Lanes hold coordinates (lane l owns coordinates r*64 + l), so the
+//    Walsh-Hadamard butterflies are cross-lane shuffles, the dense products
+//    read rows of the transposed matrices, the norms are wavefront reductions,
+//    and each key bit-plane row is one wavefront ballot.  Value bit-planes are
+//    stored per coordinate (16 token bits), which each lane accumulates in
+//    registers over the page's tokens and writes once.
 #include "tq_device.h"
 
 namespace tqi {
@@ -37,38 +38,41 @@ struct Codebooks {
   float kc[8], kt[7], vc[16], vt[15];
 };
 
-// Rotation of a wavefront-resident vector: FWHT variant y = H D x * scale,
-// dense variant y = M x * scale (M row-major d x d in global memory, x staged
-// through LDS).
-template <int D, int ROT>
-__device__ __forceinline__ void rotate(float (&x)[D / 64], const uint8_t* params, int role,
-                                       const float* dense, float* lds, int lane, float scale) {
+// x <- scale * M x for a wavefront-resident vector (lane l holds coordinates
+// r*64 + l) and a d x d matrix given transposed (mt = M^T, row-major): lane l
+// computes outputs R l .. R l + R - 1 from an R-wide slice of each row of M^T,
+// so the wavefront's loads of one step are one contiguous row; x and the
+// outputs pass through the wavefront's own LDS (no other wavefront touches it,
+// and one wavefront's LDS accesses complete in order).
+template <int D>
+__device__ __forceinline__ void rotate_dense_t(float (&x)[D / 64], const float* mt, float* lds, int lane,
+                                               float scale) {
   constexpr int R = D / 64;
-  if (ROT == TQ_ROT_FWHT) {
+  typedef float vecR __attribute__((ext_vector_type(R)));
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sign_bit(params, role, r * 64 + lane));
-    wave_fwht<R>(x, lane);
+  for (int r = 0; r < R; ++r) lds[r * 64 + lane] = x[r];
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  const vecR* col = reinterpret_cast<const vecR*>(mt) + lane;
+  vecR acc[4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] *= scale;
-  } else {
+  for (int u = 0; u < 4; ++u) acc[u] = vecR{};
+#pragma unroll 4
+  for (int j = 0; j < D; j += 4) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) lds[r * 64 + lane] = x[r];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float* row = dense + size_t(r * 64 + lane) * D;
-      float acc = 0.f;
-      for (int j = 0; j < D; j += 4) {
-        const float4 m = *reinterpret_cast<const float4*>(row + j);
-        acc = fmaf(m.x, lds[j], acc);
-        acc = fmaf(m.y, lds[j + 1], acc);
-        acc = fmaf(m.z, lds[j + 2], acc);
-        acc = fmaf(m.w, lds[j + 3], acc);
-      }
-      x[r] = acc * scale;
-    }
-    __syncthreads();
+    for (int u = 0; u < 4; ++u) acc[u] += col[size_t(j + u) * (D / R)] * lds[j + u];
   }
+  const vecR o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < R; ++k) lds[R * lane + k] = o[k];
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = lds[r * 64 + lane] * scale;
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // FWHT rotation with the role's sign bits already in registers (as masks on
@@ -82,32 +86,25 @@ __device__ __forceinline__ void fwht_rotate(float (&x)[R], const uint32_t (&sm)[
   for (int r = 0; r < R; ++r) x[r] *= scale;
 }
 
-// QJL projection w = S e: FWHT variant S = H D2 H_n D1, dense variant S = G.
-template <int D, int ROT>
-__device__ __forceinline__ void sketch(float (&e)[D / 64], const uint8_t* params, float* lds, int lane) {
-  constexpr int R = D / 64;
-  if (ROT == TQ_ROT_FWHT) {
-    rotate<D, ROT>(e, params, kRoleSketch1, nullptr, lds, lane, rsqrtf(float(D)));
-    rotate<D, ROT>(e, params, kRoleSketch2, nullptr, lds, lane, 1.0f);
-  } else {
-    const float* g = reinterpret_cast<const float*>(params + kOffDense) + size_t(D) * D;
-    rotate<D, ROT>(e, params, 0, g, lds, lane, 1.0f);
-  }
-  (void)R;
-}
-
 __device__ __forceinline__ int quantize(float y, const float* t, int n_thr) {
   int idx = 0;
   for (int j = 0; j < n_thr; ++j) idx += (t[j] < y) ? 1 : 0;
   return idx;
 }
 
+// Two wavefronts per (sequence, kv head, part): wavefront 0 quantizes the keys
+// (norm, rotation, codes, residual, QJL sketch, key words and norms, key ring
+// rows), wavefront 1 the values (norm, rotation, codes, value words and norms,
+// value ring rows), each over the same tokens; the two never wait for each
+// other.
 template <int D, int ROT>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   constexpr int R = D / 64;
   constexpr int P = 16;
-  __shared__ float lds[D];
-  const int lane = threadIdx.x;
+  __shared__ float lds_all[2][D];
+  const int lane = threadIdx.x & 63;
+  const bool values = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)) != 0;  // this wavefront's role
+  float* lds = lds_all[values ? 1 : 0];
   const CacheView& cv = a.cache;
   const int H = cv.num_kv_heads;
   int unit = blockIdx.x;
@@ -130,32 +127,30 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 
   const int mk = a.key_mse_bits, bv = a.value_bits;
   const int nkt = (1 << mk) - 1, nvt = (1 << bv) - 1;
+  // this role's codebook (keys: centroids and thresholds; values: thresholds)
   const float* kc = reinterpret_cast<const float*>(a.params + kOffKeyCentroids);
-  const float* kt = reinterpret_cast<const float*>(a.params + kOffKeyThresholds);
-  const float* vt = reinterpret_cast<const float*>(a.params + kOffValueThresholds);
-  float kcr[8], ktr[7], vtr[15];
+  const float* thr = reinterpret_cast<const float*>(a.params + (values ? kOffValueThresholds : kOffKeyThresholds));
+  float kcr[8], tr[15];
 #pragma unroll
   for (int j = 0; j < 8; ++j) kcr[j] = kc[j];
 #pragma unroll
-  for (int j = 0; j < 7; ++j) ktr[j] = kt[j];
-#pragma unroll
-  for (int j = 0; j < 15; ++j) vtr[j] = vt[j];
-  const float* pik = reinterpret_cast<const float*>(a.params + kOffDense);
-  const float* piv = pik + size_t(2) * D * D;
+  for (int j = 0; j < 15; ++j) tr[j] = thr[j];
   const float rot_scale = (ROT == TQ_ROT_FWHT) ? rsqrtf(float(D)) : 1.0f;
-  // FWHT variant: the four roles' sign bits, requested with the other
-  // parameters rather than after the page stores (which the compiler cannot
-  // move them past)
-  uint32_t sgn_k[R], sgn_s1[R], sgn_s2[R], sgn_v[R];
+  // FWHT variant: this role's sign bits, requested with the other parameters
+  // rather than after the page stores (which the compiler cannot move them past)
+  uint32_t sgn_a[R], sgn_b[R], sgn_c[R];
   if constexpr (ROT == TQ_ROT_FWHT) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      sgn_k[r] = sign_bit(a.params, kRoleKeyRot, r * 64 + lane) << 31;
-      sgn_s1[r] = sign_bit(a.params, kRoleSketch1, r * 64 + lane) << 31;
-      sgn_s2[r] = sign_bit(a.params, kRoleSketch2, r * 64 + lane) << 31;
-      sgn_v[r] = sign_bit(a.params, kRoleValueRot, r * 64 + lane) << 31;
+      sgn_a[r] = sign_bit(a.params, values ? kRoleValueRot : kRoleKeyRot, r * 64 + lane) << 31;
+      sgn_b[r] = sign_bit(a.params, kRoleSketch1, r * 64 + lane) << 31;
+      sgn_c[r] = sign_bit(a.params, kRoleSketch2, r * 64 + lane) << 31;
     }
   }
+  const float* rot_t = reinterpret_cast<const float*>(a.params + dense_t_offset(D, values ? 3 : 0));
+  const float* g_t = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 2));
+  const void* rows = values ? a.v_new : a.k_new;
+  uint16_t* ring = values ? cv.v_window : cv.k_window;
 
   const size_t plane_bytes = size_t(P) * D / 8;
   for (int pg = start / P + part; pg * P < new_len; pg += a.parts) {
@@ -183,7 +178,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         old[p][r] = 0u;
-        if (page_ok && keep16 != 0u && p < bv && !(lane & 1))
+        if (values && page_ok && keep16 != 0u && p < bv && !(lane & 1))
           old[p][r] = reinterpret_cast<const uint32_t*>(vb)[((r * 64 + lane) / 2) * bv + p];
       }
 
@@ -192,14 +187,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const int t = pos - pg * P;
       const size_t base = (tok * H + h) * D;
       const bool in_window = W > 0 && pos >= new_len - W;
-      // ---------------- key (the value row is requested with it)
-      float x[R], xin[R], vin[R];
+      float x[R], xin[R];
       float ss = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        xin[r] = load_elem(a.k_new, a.dtype, base + r * 64 + lane);
-        vin[r] = load_elem(a.v_new, a.dtype, base + r * 64 + lane);
-      }
+      for (int r = 0; r < R; ++r) xin[r] = load_elem(rows, a.dtype, base + r * 64 + lane);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         x[r] = xin[r];
@@ -209,89 +200,76 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const float nu = sqrtf(ss);
       const bool zero = !(nu >= kZeroNorm);
       const float inv = zero ? 0.f : 1.0f / nu;
-      if constexpr (ROT == TQ_ROT_FWHT) fwht_rotate<R>(x, sgn_k, lane, rot_scale * inv);
-      else rotate<D, ROT>(x, a.params, kRoleKeyRot, pik, lds, lane, rot_scale * inv);
-      int idx[R];
-      float e[R];
-      float es = 0.f;
+      if constexpr (ROT == TQ_ROT_FWHT) fwht_rotate<R>(x, sgn_a, lane, rot_scale * inv);
+      else rotate_dense_t<D>(x, rot_t, lds, lane, rot_scale * inv);
+      if (!values) {
+        // ---------------- key
+        int idx[R];
+        float e[R];
+        float es = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        idx[r] = zero ? 0 : quantize(x[r], ktr, nkt);
-        float c = kcr[0];
+        for (int r = 0; r < R; ++r) {
+          idx[r] = zero ? 0 : quantize(x[r], tr, nkt);
+          float c = kcr[0];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) c = (idx[r] == j) ? kcr[j] : c;
-        e[r] = zero ? 0.f : x[r] - c;
-        es = fmaf(e[r], e[r], es);
-      }
-      es = wave_sum(es);
-      const float gamma = sqrtf(es);
-      if constexpr (ROT == TQ_ROT_FWHT) {
-        fwht_rotate<R>(e, sgn_s1, lane, rsqrtf(float(D)));
-        fwht_rotate<R>(e, sgn_s2, lane, 1.0f);
-      } else {
-        sketch<D, ROT>(e, a.params, lds, lane);
-      }
-      if (page_ok) {
-        // token row: for each 32-coordinate group, the words of all planes
-        uint32_t words[4];
+          for (int j = 1; j < 8; ++j) c = (idx[r] == j) ? kcr[j] : c;
+          e[r] = zero ? 0.f : x[r] - c;
+          es = fmaf(e[r], e[r], es);
+        }
+        es = wave_sum(es);
+        const float gamma = sqrtf(es);
+        // QJL projection w = S e: FWHT variant S = H D2 H_n D1, dense variant S = G
+        if constexpr (ROT == TQ_ROT_FWHT) {
+          fwht_rotate<R>(e, sgn_b, lane, rsqrtf(float(D)));
+          fwht_rotate<R>(e, sgn_c, lane, 1.0f);
+        } else {
+          rotate_dense_t<D>(e, g_t, lds, lane, 1.0f);
+        }
+        if (page_ok) {
+          // token row: for each 32-coordinate group, the words of all planes
+          uint32_t words[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) words[p] = 0;
+          for (int p = 0; p < 4; ++p) words[p] = 0;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (p > mk) break;
+          for (int p = 0; p < 4; ++p) {
+            if (p > mk) break;
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const bool bit = (p < mk) ? (((idx[r] >> p) & 1) != 0) : (!zero && e[r] < 0.f);
-            const uint64_t m = __ballot(bit);
-            if ((lane >> 1) == r) words[p] = (lane & 1) ? uint32_t(m >> 32) : uint32_t(m);
+            for (int r = 0; r < R; ++r) {
+              const bool bit = (p < mk) ? (((idx[r] >> p) & 1) != 0) : (!zero && e[r] < 0.f);
+              const uint64_t m = __ballot(bit);
+              if ((lane >> 1) == r) words[p] = (lane & 1) ? uint32_t(m >> 32) : uint32_t(m);
+            }
+          }
+          if (lane < D / 32) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * (D / 32) * (mk + 1) * 4) + lane * (mk + 1);
+            for (int p = 0; p <= mk; ++p) dst[p] = words[p];
+          }
+          if (lane == 0) {
+            float* norms = reinterpret_cast<float*>(kb + size_t(mk + 1) * plane_bytes) + 2 * t;
+            norms[0] = zero ? 0.f : nu;
+            norms[1] = zero ? 0.f : gamma;
           }
         }
-        if (lane < D / 32) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(kb + size_t(t) * (D / 32) * (mk + 1) * 4) + lane * (mk + 1);
-          for (int p = 0; p <= mk; ++p) dst[p] = words[p];
+      } else {
+        // ---------------- value
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int vi = zero ? 0 : quantize(x[r], tr, nvt);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) vmask[p][r] |= uint32_t((vi >> p) & 1) << t;
         }
-        if (lane == 0) {
-          float* norms = reinterpret_cast<float*>(kb + size_t(mk + 1) * plane_bytes) + 2 * t;
-          norms[0] = zero ? 0.f : nu;
-          norms[1] = zero ? 0.f : gamma;
+        if (page_ok && lane == 0) {
+          float* norms = reinterpret_cast<float*>(vb + size_t(bv) * plane_bytes);
+          norms[t] = zero ? 0.f : nu;
         }
       }
       if (in_window) {
-        uint16_t* kw = cv.k_window + ((size_t(slot) * H + h) * W + (pos % W)) * D;
+        uint16_t* rw = ring + ((size_t(slot) * H + h) * W + (pos % W)) * D;
 #pragma unroll
-        for (int r = 0; r < R; ++r) kw[r * 64 + lane] = float_to_f16_bits(xin[r]);
-      }
-      // ---------------- value
-      ss = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        xin[r] = vin[r];
-        x[r] = xin[r];
-        ss = fmaf(x[r], x[r], ss);
-      }
-      ss = wave_sum(ss);
-      const float vnu = sqrtf(ss);
-      const bool vzero = !(vnu >= kZeroNorm);
-      const float vinv = vzero ? 0.f : 1.0f / vnu;
-      if constexpr (ROT == TQ_ROT_FWHT) fwht_rotate<R>(x, sgn_v, lane, rot_scale * vinv);
-      else rotate<D, ROT>(x, a.params, kRoleValueRot, piv, lds, lane, rot_scale * vinv);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int vi = vzero ? 0 : quantize(x[r], vtr, nvt);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) vmask[p][r] |= uint32_t((vi >> p) & 1) << t;
-      }
-      if (page_ok && lane == 0) {
-        float* norms = reinterpret_cast<float*>(vb + size_t(bv) * plane_bytes);
-        norms[t] = vzero ? 0.f : vnu;
-      }
-      if (in_window) {
-        uint16_t* vw = cv.v_window + ((size_t(slot) * H + h) * W + (pos % W)) * D;
-#pragma unroll
-        for (int r = 0; r < R; ++r) vw[r * 64 + lane] = float_to_f16_bits(xin[r]);
+        for (int r = 0; r < R; ++r) rw[r * 64 + lane] = float_to_f16_bits(xin[r]);
       }
     }
-    if (page_ok) {
+    if (values && page_ok) {
       // token bits below `lo` were written by earlier calls; keep them.  Value
       // words pair coordinates 2i (low half) and 2i + 1 (high half).
       const uint32_t keep = keep16 | (keep16 << 16);
@@ -1187,7 +1165,7 @@ hipError_t launch_tok(const AppendArgs& a, int units, hipStream_t st) {
 
 template <int D, int ROT>
 hipError_t launch(const AppendArgs& a, int units, hipStream_t st) {
-  hipLaunchKernelGGL((append_kernel<D, ROT>), dim3(units), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((append_kernel<D, ROT>), dim3(units), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1197,9 +1175,11 @@ hipError_t launch(const AppendArgs& a, int units, hipStream_t st) {
 // per token has the shorter latency: one lane would otherwise do a whole head
 // vector alone while the other 63 idle.
 constexpr int kTokenLaneMinNew = 32;
-// Dense rotation: the matrix-core kernel at any append size (even a single
-// token's tile costs less than the three d x d GEMVs of the wavefront-per-token
-// kernel, which stream the matrices with long dependent load chains).
+// Dense rotation: the matrix-core kernel at any append size.  A single token's
+// 64-token tile (38 us at head_dim 256) still beats the wavefront-per-token
+// kernel, whose one wavefront per role streams each d x d matrix with only a
+// few row loads in flight (137 us for a one-token-per-sequence step at
+// head_dim 256, with coalesced rows of the transposed matrices).
 constexpr int kDenseMatrixMinNew = 1;
 
 int launch_append(const tq_config& cfg, const AppendArgs& args, int num_seqs, int max_new, void* stream) {

@@ -310,6 +310,11 @@ void build_params(const tq_config& cfg, uint8_t* blob) {
       if (m != 1) g = haar_from_gaussian(std::move(g), d);
       for (size_t i = 0; i < size_t(d) * d; ++i) dst[size_t(m) * d * d + i] = float(g[i]);
       if (m < 2) exact[m] = g;
+      if (m > 0) {  // G^T and Pi_V^T for the short appends
+        float* t = reinterpret_cast<float*>(blob + dense_t_offset(d, m + 1));
+        for (int r = 0; r < d; ++r)
+          for (int c = 0; c < d; ++c) t[size_t(c) * d + r] = dst[size_t(m) * d * d + size_t(r) * d + c];
+      }
       // fp16 hi / lo split of the scaled fp32 matrix for the matrix cores
       _Float16* hi = reinterpret_cast<_Float16*>(blob + dense16_offset(d, m));
       _Float16* lo = hi + size_t(d) * d;

@@ -64,17 +64,18 @@ struct ParamsHeader {
 static_assert(sizeof(ParamsHeader) == 64, "header is 64 bytes");
 
 // Dense variant after the header tables: Pi_K, G, Pi_V as fp32 row-major;
-// their fp16 hi / lo splits; then Pi_K^T and (G Pi_K)^T as fp32 row-major
-// (the decode's query preparation: both products of the query in one pass,
-// with a wavefront's loads of one step contiguous).
+// their fp16 hi / lo splits; then, as fp32 row-major, Pi_K^T and (G Pi_K)^T
+// (the decode's query preparation: both products of the query in one pass)
+// and G^T, Pi_V^T (the short appends' products): a wavefront's loads of one
+// step of a product read one contiguous row.
 inline size_t params_bytes(int d, int rotation) {
   return kOffDense + (rotation == TQ_ROT_DENSE ? size_t(d) * d * (3 * sizeof(float) + 3 * 2 * sizeof(uint16_t) +
-                                                                  2 * sizeof(float))
+                                                                  4 * sizeof(float))
                                                : 0);
 }
 // byte offset of the fp16 split of dense matrix m (0 Pi_K, 1 G, 2 Pi_V); lo follows hi
 constexpr size_t dense16_offset(int d, int m) { return kOffDense + size_t(3) * d * d * 4 + size_t(m) * d * d * 4; }
-// byte offset of the query preparation's fp32 matrix m (0 Pi_K^T, 1 (G Pi_K)^T)
+// byte offset of the transposed fp32 matrix m (0 Pi_K^T, 1 (G Pi_K)^T, 2 G^T, 3 Pi_V^T)
 constexpr size_t dense_t_offset(int d, int m) { return kOffDense + size_t(6) * d * d * 4 + size_t(m) * d * d * 4; }
 constexpr float kDense16Scale[3] = {1024.f, 256.f, 1024.f};
 

@@ -82,6 +82,9 @@ def test_host_params_match_oracle(d, kb, vb, rot):
         assert np.abs(Mt[0] - T.pk.T).max() < 1e-6
         gp = (T.g @ T.pk).T
         assert np.abs(Mt[1] - gp).max() <= 2.0 ** -23 * np.abs(gp).max() * 2
+        # G^T and Pi_V^T for the short appends: exact transposes of the fp32 matrices
+        Mt2 = f[(2048 + 32 * d * d) // 4:(2048 + 40 * d * d) // 4].reshape(2, d, d)
+        assert np.array_equal(Mt2[0], M[1].T) and np.array_equal(Mt2[1], M[2].T)
 
 
 def test_size_queries_match_layout():
@@ -92,7 +95,7 @@ def test_size_queries_match_layout():
         f = tq.Config(d, 8, 2, kb, vb)
         assert tqa.key_block_bytes(cfg) == layout.key_block_bytes(f)
         assert tqa.value_block_bytes(cfg) == layout.value_block_bytes(f)
-        assert tqa.params_bytes(cfg) == 2048 + (32 * d * d if rot == "dense" else 0)
+        assert tqa.params_bytes(cfg) == 2048 + (40 * d * d if rot == "dense" else 0)
         ws = tqa.decode_workspace_bytes(cfg, 3, 1000)
         # at least one partial record (max, denominator, d sums) per (sequence, query head)
         # for the compressed part and one for the window, in float32
