@@ -1399,6 +1399,18 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   // from the lanes instead of being read again (every caller's record index
   // is uniform across its wavefront).
   const bool in_lanes = (WIDE || ROT == TQ_ROT_DENSE) && ns + NWR <= 128;
+  // this thread's coordinates of the window records' sums, requested first so
+  // that they arrive with the records' maxima (FWHT: r * 64 + lane; dense:
+  // tid % D, used by the first slice)
+  constexpr int NWC = ROT == TQ_ROT_DENSE ? 1 : R;
+  float wvals[kWindowRecords][NWC];
+#pragma unroll
+  for (int j = 0; j < kWindowRecords; ++j)
+#pragma unroll
+    for (int r = 0; r < NWC; ++r) {
+      const int c = ROT == TQ_ROT_DENSE ? tid % D : r * 64 + lane;
+      wvals[j][r] = j < NWR ? rec_of(ns + j)[2 + c] : 0.f;
+    }
   float M = -INFINITY, l = 0.f, wl[2] = {0.f, 0.f};
   if (in_lanes) {
     // lane t holds records t and t + 64
@@ -1434,12 +1446,12 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   float fw[kWindowRecords];
 #pragma unroll
   for (int j = 0; j < kWindowRecords; ++j) fw[j] = j < NWR ? weight(ns + j) : 0.f;
-  // the window records' weighted value sum at coordinate c
-  auto window_sum = [&](int c) {
+  // the window records' weighted value sum at this thread's coordinate i
+  // (index into wvals)
+  auto window_sum = [&](int i) {
     float aw = 0.f;
 #pragma unroll
-    for (int j = 0; j < kWindowRecords; ++j)
-      if (fw[j] != 0.f) aw = fmaf(fw[j], rec_of(ns + j)[2 + c], aw);
+    for (int j = 0; j < kWindowRecords; ++j) aw = fmaf(fw[j], wvals[j][i], aw);
     return aw;
   };
   if constexpr (ROT == TQ_ROT_FWHT) {
@@ -1495,7 +1507,7 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
     for (int r = 0; r < R; ++r) {
       const int c = r * 64 + lane;
       const float o = rotated ? apply_sign(ar[r] * rsqrtf(float(D)), sign_bit(a.params, kRoleValueRot, c)) : ar[r];
-      const float aw = window_sum(c);
+      const float aw = window_sum(r);
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
   } else {
@@ -1551,7 +1563,7 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
       float o = 0.f;
 #pragma unroll
       for (int q = 0; q < KQ; ++q) o += buf[q * D + c];
-      const float aw = window_sum(c);
+      const float aw = window_sum(0);
       a.out[row * D + c] = l > 0.f ? (o + aw) / l : 0.f;
     }
   }
