@@ -21,17 +21,19 @@
 //   values^T [16 coords x 16 (head, part)] = planes^T [16 coords x 128 tokens, fp4] x W [128 tokens x 16, fp8]
 //     for every value bit-plane product; 128 tokens (8 pages) per MFMA.
 //
-// Three launches:
+// Launches:
 //   decode_prep: per (sequence, kv head), rotate and sketch the GQA group's
-//     queries and store their fp8 operand rows in the workspace;
+//     queries and store their fp8 operand rows in the workspace (skipped
+//     with the FWHT rotation and few splits per (sequence, kv head): each
+//     split work item then builds its query operands itself, in LDS);
 //   decode_split: one workgroup of NW wavefronts per (sequence, kv head,
-//     context split).  Per block of 128 tokens the wavefronts score disjoint
-//     pages, agree on the block maximum, write the fp8 parts of the softmax
-//     weights to LDS in the value operand's order and each accumulates its
-//     coordinate blocks of the value tiles.  The next block's page data is
-//     requested as soon as the current block's registers are consumed.  One
-//     extra split per (sequence, kv head) attends the fp16 recent window
-//     exactly;
+//     context split).  Per block of 128 tokens the wavefronts score
+//     disjoint pages, agree on the block maximum, write the fp8 parts of the
+//     softmax weights to LDS in the value operand's order and each
+//     accumulates its coordinate blocks of the value tiles.  The next block's
+//     page data is requested as soon as the current block's registers are
+//     consumed.  Up to four extra work items per (sequence, kv head) attend
+//     the fp16 recent window exactly;
 //   decode_combine: per (sequence, query head), merge the splits by
 //     log-sum-exp, rotate the compressed part back once, add the window part,
 //     normalise and store.
@@ -216,221 +218,151 @@ __device__ void check_sequence(const DecodeArgs& a, int s, int tid, int nthreads
 }
 
 // ---------------------------------------------------------------------------- query operands
-// One workgroup per (sequence, kv head); wavefront h rotates and sketches query
-// head h of the GQA group in registers (FWHT variant) and reduces its operand
-// scale and affine constants; then the lane-major operand images are built in
-// LDS and copied out in 16-byte pieces.
-// EXT: each half of the coordinates takes its own plane coefficients (zero
-// for products of planes the half does not store), the sketch is skipped for
-// scale-corrected keys, and the unrotated query is stored for the sidecar.
-template <int D, int MK, int ROT, bool EXT>
-__global__ __launch_bounds__(ROT == TQ_ROT_DENSE ? 1024 : 256) void decode_prep_kernel(DecodeArgs a) {
-  // FWHT variant: one wavefront per query head; dense variant: 1024 threads,
-  // so that the matrix-vector products have enough wavefronts to hide latency
-  constexpr int KP = num_planes(MK), KH = D / 128, R = D / 64, T = ROT == TQ_ROT_DENSE ? 1024 : 256;
-  constexpr int KQ = T / D;  // dense: slices of the contraction per output row
-  static_assert(T >= 64 * kMaxG, "a wavefront per query head of the group");
-  // operand images; before them (dense variant) the products' partial sums per slice
-  constexpr int kImgBytes = (KP + 1) * KH * 2048;
-  constexpr int kRedBytes = ROT == TQ_ROT_DENSE ? 2 * KQ * kMaxG * D * 4 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t img[kImgBytes > kRedBytes ? kImgBytes : kRedBytes];
-  float* red = reinterpret_cast<float*>(img);
-  __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
-  __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
-  __shared__ float coef_k[EXT ? 32 : 16], qscale[kMaxG];  // EXT: lower half [0, 16), upper [16, 32)
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.cache.num_kv_heads;
-  const int G = a.num_q_heads / H;
-  const int s = blockIdx.x / H, hk = blockIdx.x % H;
-  uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
-  float* dst_raw = reinterpret_cast<float*>(dst + (KP + 1) * KH * 2048 + 256);  // EXT only
-  const bool qjl = !EXT || a.cache.codec.qjl;
-  auto load_coef = [&]() {
-    if (tid < (EXT ? 32 : 16))
-      coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
-  };
-  if (a.cache.status != nullptr && hk == 0) check_sequence(a, s, tid, T);
-  // scores come out in base-2 logits: the softmax scale times log2(e) rides on
-  // both query operands, and the QJL constant sqrt(pi/2)/d on the sketch one
+// Operand region of one (sequence, kv head): the lane-major fp8 images
+// [plane][half] (rows 4 h + part), then a 256-byte tail of 32-bit words:
+// [0, 16) the E8M0 scales of rows 4 h + p, [16, 20) the key-plane constants,
+// [20, 24) the QJL constants of heads 0-3, [24, 28) each head's operand scale
+// (used while the images are built).
+template <int D, int MK>
+__host__ __device__ constexpr int image_bytes() { return (num_planes(MK) + 1) * (D / 128) * 2048; }
+
+// Rotated query qt = H_n D_K q of head h of the GQA group and its sketch
+// qh = H D2 H_n D1 qt ([Reconstruction] section 6; H_n the orthonormal
+// Walsh-Hadamard transform), in base-2 logit units (the softmax scale times
+// log2(e), and the sketch also the QJL constant sqrt(pi/2)/d), to LDS rows
+// q_rot[h] and q_sk[h]: zeros past the group, and no sketch for keys without
+// the QJL plane.  EXT also keeps the unrotated query in logit units in raw[h]
+// for the sidecar entries.  One wavefront per head.
+template <int D, bool EXT>
+__device__ __forceinline__ void query_fwht(const DecodeArgs& a, size_t qrow0, int G, int h, int lane, bool qjl,
+                                           float* q_rot, float* q_sk, float* raw) {
+  constexpr int R = D / 64;
   const float s2 = a.scale * 1.4426950408889634f;
   const float s2q = s2 * kQjlConst / float(D);
-  const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
-  if (ROT == TQ_ROT_FWHT) {
-    // qt = H_n D_K q;  qh = H D2 H_n D1 qt
-    // every global load first (one uniform dtype branch), so that they are in
-    // flight together
-    float x[R], y[R];
-    uint32_t sgk[R], sg1[R], sg2[R];
-    const size_t qb = (qrow0 + wv) * D + lane;
-    if (wv >= G) {
+  // every global load first (one uniform dtype branch), so that they are in
+  // flight together
+  float x[R], y[R];
+  uint32_t sgk[R], sg1[R], sg2[R];
+  const size_t qb = (qrow0 + h) * D + lane;
+  if (h >= G) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) x[r] = 0.f;
-    } else if (a.q_dtype == TQ_F32) {
+    for (int r = 0; r < R; ++r) x[r] = 0.f;
+  } else if (a.q_dtype == TQ_F32) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) x[r] = static_cast<const float*>(a.q)[qb + r * 64];
-    } else {
-      uint16_t qbits[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) qbits[r] = static_cast<const uint16_t*>(a.q)[qb + r * 64];
-      const bool bf = a.q_dtype == TQ_BF16;
-#pragma unroll
-      for (int r = 0; r < R; ++r) x[r] = bf ? bf16_bits_to_float(qbits[r]) : f16_bits_to_float(qbits[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int c = r * 64 + lane;
-      sgk[r] = sign_bit(a.params, kRoleKeyRot, c);
-      sg1[r] = sign_bit(a.params, kRoleSketch1, c);
-      sg2[r] = sign_bit(a.params, kRoleSketch2, c);
-    }
-    load_coef();
-    if constexpr (EXT) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) dst_raw[wv * D + r * 64 + lane] = x[r] * s2;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sgk[r]);
-    wave_fwht<R>(x, lane);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      x[r] *= rsqrtf(float(D));
-      y[r] = apply_sign(x[r], sg1[r]);
-    }
-    if (qjl) {
-      wave_fwht<R>(y, lane);
-#pragma unroll
-      for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
-      wave_fwht<R>(y, lane);
-    } else {
-#pragma unroll
-      for (int r = 0; r < R; ++r) y[r] = 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      q_rot[wv * D + r * 64 + lane] = x[r] * s2;
-      q_sk[wv * D + r * 64 + lane] = y[r] * s2q;
-    }
-    __syncthreads();
+    for (int r = 0; r < R; ++r) x[r] = static_cast<const float*>(a.q)[qb + r * 64];
   } else {
-    // qt = Pi_K q and qh = G Pi_K q in one pass over q, from the transposed
-    // matrices Pi_K^T and (G Pi_K)^T: thread (i, k) sums slice k of the
-    // products for output coordinate i of the whole group, so that the threads
-    // of a wavefront read consecutive entries of a matrix row (each entry is
-    // read once); the slices meet in LDS.
-    load_coef();
-    for (int i = tid; i < kMaxG * D; i += T) {
-      const int g = i / D;
-      q_rot[i] = g < G ? load_elem(a.q, a.q_dtype, qrow0 * D + i) : 0.f;
-      if constexpr (EXT) dst_raw[i] = q_rot[i] * s2;
+    uint16_t qbits[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) qbits[r] = static_cast<const uint16_t*>(a.q)[qb + r * 64];
+    const bool bf = a.q_dtype == TQ_BF16;
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = bf ? bf16_bits_to_float(qbits[r]) : f16_bits_to_float(qbits[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = r * 64 + lane;
+    sgk[r] = sign_bit(a.params, kRoleKeyRot, c);
+    sg1[r] = sign_bit(a.params, kRoleSketch1, c);
+    sg2[r] = sign_bit(a.params, kRoleSketch2, c);
+  }
+  if constexpr (EXT) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[h * D + r * 64 + lane] = x[r] * s2;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sgk[r]);
+  wave_fwht<R>(x, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    x[r] *= rsqrtf(float(D));
+    y[r] = apply_sign(x[r], sg1[r]);
+  }
+  if (qjl) {
+    wave_fwht<R>(y, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
+    wave_fwht<R>(y, lane);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    q_rot[h * D + r * 64 + lane] = x[r] * s2;
+    q_sk[h * D + r * 64 + lane] = y[r] * s2q;
+  }
+}
+
+// Head h's operand constants (one wavefront): one power of two 2^e bringing
+// the larger of its key-plane and QJL operands' largest entry into (128, 256]
+// (the smaller operand keeps the four parts' precision far below the
+// tolerance), undone by the score MFMA's per-row operand scale together with
+// the part weight 16^-p; and the constants of the affine fp4 encoding of the
+// key bits (coordinate c falls in element group c % 4): the sums of the
+// operands over the coordinates with c % 4 < 3, which seed the accumulators.
+// coef: the key-plane coefficients (EXT: lower half [0, 16), upper [16, 32));
+// tail: the region's tail words.
+// EXT: each half of the coordinates takes its own plane coefficients (zero
+// for products of planes the half does not store).
+template <int D, int MK, bool EXT>
+__device__ __forceinline__ void head_constants(const float* q_rot, const float* q_sk, const float* coef, int h,
+                                               int lane, uint32_t* tail) {
+  constexpr int KP = num_planes(MK), R = D / 64;
+  // per half (one half unless EXT): the sum and the largest magnitude of the
+  // plane coefficients
+  float csum[2] = {0.f, 0.f}, cmax[2] = {0.f, 0.f};
+#pragma unroll
+  for (int hf = 0; hf < (EXT ? 2 : 1); ++hf)
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const float cf = coef[16 * hf + odd_subset(MK, i)];
+      csum[hf] += cf;
+      cmax[hf] = fmaxf(cmax[hf], fabsf(cf));
     }
-    __syncthreads();
-    {
-      constexpr int J = D / KQ;  // contraction slice per thread
-      const int i = tid % D, k = tid / D, k0 = k * J;
-      const float* m0 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 0)) + size_t(k0) * D + i;
-      const float* m1 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 1)) + size_t(k0) * D + i;
-      float ar[kMaxG] = {0.f, 0.f, 0.f, 0.f}, as[kMaxG] = {0.f, 0.f, 0.f, 0.f};
-      if (qjl) {
-#pragma unroll 16
-        for (int j = 0; j < J; ++j) {
-          const float u = m0[size_t(j) * D], v = m1[size_t(j) * D];
+  float qm = 0.f, qh = 0.f, sm = 0.f, sh = 0.f;
 #pragma unroll
-          for (int h = 0; h < kMaxG; ++h) {
-            const float x = q_rot[h * D + k0 + j];
-            ar[h] = fmaf(u, x, ar[h]);
-            as[h] = fmaf(v, x, as[h]);
-          }
-        }
-      } else {
-#pragma unroll 16
-        for (int j = 0; j < J; ++j) {
-          const float u = m0[size_t(j) * D];
-#pragma unroll
-          for (int h = 0; h < kMaxG; ++h) ar[h] = fmaf(u, q_rot[h * D + k0 + j], ar[h]);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < kMaxG; ++h) {
-        red[(k * kMaxG + h) * D + i] = ar[h];
-        red[((KQ + k) * kMaxG + h) * D + i] = as[h];
-      }
-      __syncthreads();
-      for (int o = tid; o < kMaxG * D; o += T) {
-        float vr = 0.f, vs = 0.f;
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-          vr += red[q * kMaxG * D + o];
-          vs += red[(KQ + q) * kMaxG * D + o];
-        }
-        q_rot[o] = vr * s2;
-        q_sk[o] = vs * s2q;
-      }
-      __syncthreads();
+  for (int r = 0; r < R; ++r) {
+    const int c = r * 64 + lane;
+    const int hf = EXT && c >= D / 2 ? 1 : 0;
+    const float f = fabsf(fp4_affine_factor(c & 3));
+    const float xr = q_rot[h * D + c], xs = q_sk[h * D + c];
+    qm = fmaxf(qm, f * fabsf(xr) * (EXT ? cmax[hf] : 1.f));
+    qh = fmaxf(qh, f * fabsf(xs));
+    if ((c & 3) != 3) {
+      sm += EXT ? xr * csum[hf] : xr;
+      sh += xs;
     }
   }
-  // Per head (wavefront wv): one power of two 2^e bringing the larger of its
-  // key-plane and QJL operands' largest entry into (128, 256] (the smaller
-  // operand keeps the four parts' precision far below the tolerance), undone
-  // by the score MFMA's per-row operand scale together with the part weight
-  // 16^-p; and the constants of the affine fp4 encoding of the key bits
-  // (coordinate c falls in element group c % 4): the sums of the operands over
-  // the coordinates with c % 4 < 3, which seed the accumulators.  Tail: int32
-  // [0, 16) E8M0 scales of rows 4 h + p; float [16, 20) key-plane constants,
-  // [20, 24) QJL constants.
-  if (wv < kMaxG) {
-    // per half (one half unless EXT): the sum and the largest magnitude of
-    // the plane coefficients
-    float csum[2] = {0.f, 0.f}, cmax[2] = {0.f, 0.f};
-#pragma unroll
-    for (int hf = 0; hf < (EXT ? 2 : 1); ++hf)
-#pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const float cf = coef_k[16 * hf + odd_subset(MK, i)];
-        csum[hf] += cf;
-        cmax[hf] = fmaxf(cmax[hf], fabsf(cf));
-      }
-    float qm = 0.f, qh = 0.f, sm = 0.f, sh = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int c = r * 64 + lane;
-      const int hf = EXT && c >= D / 2 ? 1 : 0;
-      const float f = fabsf(fp4_affine_factor(c & 3));
-      const float xr = q_rot[wv * D + c], xs = q_sk[wv * D + c];
-      qm = fmaxf(qm, f * fabsf(xr) * (EXT ? cmax[hf] : 1.f));
-      qh = fmaxf(qh, f * fabsf(xs));
-      if ((c & 3) != 3) {
-        sm += EXT ? xr * csum[hf] : xr;
-        sh += xs;
-      }
-    }
-    qm = wave_max(qm);
-    qh = wave_max(qh);
-    sm = wave_sum(sm);
-    sh = wave_sum(sh);
-    const int e = fp8_range_exp(fmaxf(EXT ? qm : qm * cmax[0], qh));
-    if (lane == 0) {
-      qscale[wv] = ldexpf(1.f, e);
-      int32_t* tail_i = reinterpret_cast<int32_t*>(dst + (KP + 1) * KH * 2048);
-      float* tail_f = reinterpret_cast<float*>(tail_i + 16);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) tail_i[4 * wv + p] = kScaleOne - e - 4 * p;
-      tail_f[wv] = EXT ? sm : sm * csum[0];
-      tail_f[kMaxG + wv] = sh;
-    }
+  qm = wave_max(qm);
+  qh = wave_max(qh);
+  sm = wave_sum(sm);
+  sh = wave_sum(sh);
+  const int e = fp8_range_exp(fmaxf(EXT ? qm : qm * cmax[0], qh));
+  if (lane < 4) tail[4 * h + lane] = uint32_t(kScaleOne - e - 4 * lane);
+  if (lane == 0) {
+    tail[16 + h] = __float_as_uint(EXT ? sm : sm * csum[0]);
+    tail[16 + kMaxG + h] = __float_as_uint(sh);
+    tail[16 + 2 * kMaxG + h] = __float_as_uint(ldexpf(1.f, e));
   }
-  __syncthreads();
-  // Operand images [plane][half], rows 4 h + part, built in LDS and stored
-  // in 16-byte pieces.  Coordinate c sits in key word wd = c / 32 at bit
-  // c % 32; the word feeds half (KH == 2 ? wd & 1 : 0) at K group
-  // (KH == 2 ? wd >> 1 : wd), fp4 element fp4_bit_elem(c % 32).  Coordinates
-  // c and c + 4 (c % 8 < 4) land on adjacent bytes, so each thread splits such
-  // a pair at once and stores 16 bits per part row.
+}
+
+// The operand images [plane][half], rows 4 h + part, from q_rot and q_sk
+// with T threads.  Coordinate c sits in key word wd = c / 32 at bit c % 32;
+// the word feeds half (KH == 2 ? wd & 1 : 0) at K group
+// (KH == 2 ? wd >> 1 : wd), fp4 element fp4_bit_elem(c % 32).  Coordinates c
+// and c + 4 (c % 8 < 4) land on adjacent bytes, so each thread splits such a
+// pair at once and stores 16 bits per part row.
+template <int D, int MK, bool EXT, int T>
+__device__ __forceinline__ void build_images(const float* q_rot, const float* q_sk, const float* coef,
+                                             const uint32_t* tail, uint8_t* img, int tid) {
+  constexpr int KP = num_planes(MK), KH = D / 128;
   for (int i = tid; i < (KP + 1) * kMaxG * (D / 2); i += T) {
     const int pl = i / (kMaxG * D / 2), rem = i % (kMaxG * D / 2), h = rem / (D / 2), cp = rem % (D / 2);
     const int c = 8 * (cp >> 2) + (cp & 3);
     const float* src = (pl < KP ? q_rot : q_sk) + h * D;
     const int chf = EXT && c >= D / 2 ? 16 : 0;
-    const float mul = fp4_affine_factor(c & 3) * qscale[h] * (pl < KP ? coef_k[chf + odd_subset(MK, pl)] : 1.f);
+    const float mul = fp4_affine_factor(c & 3) * __uint_as_float(tail[16 + 2 * kMaxG + h]) *
+                      (pl < KP ? coef[chf + odd_subset(MK, pl)] : 1.f);
     uint32_t lo, hi;
     fp8_split4_pair(src[c] * mul, src[c + 4] * mul, 0u, 0u, lo, hi);
     const int wd = c / 32;
@@ -443,8 +375,109 @@ __global__ __launch_bounds__(ROT == TQ_ROT_DENSE ? 1024 : 256) void decode_prep_
     im[16] = uint16_t(hi);
     im[24] = uint16_t(hi >> 16);
   }
+}
+
+// One workgroup per (sequence, kv head): the GQA group's rotated queries and
+// sketches (FWHT: a wavefront per head; dense: the products qt = Pi_K q and
+// qh = G Pi_K q of the whole group over 1024 threads), the heads' constants
+// and the operand images, built in LDS and copied to the workspace in 16-byte
+// pieces.  EXT stores the unrotated query after the tail for the sidecar
+// entries.
+template <int ROT>
+__host__ __device__ constexpr int prep_threads() { return ROT == TQ_ROT_DENSE ? 1024 : 256; }
+template <int D, int MK, int ROT, bool EXT>
+__global__ __launch_bounds__(prep_threads<ROT>()) void decode_prep_kernel(DecodeArgs a) {
+  // dense: 1024 threads, so that the matrix-vector products have enough
+  // wavefronts to hide latency
+  constexpr int T = prep_threads<ROT>();
+  static_assert(T >= 64 * kMaxG, "a wavefront per query head of the group");
+  constexpr int KQ = T / D;  // dense: slices of the contraction per output row
+  // operand images and tail; before them (dense) the products' partial sums per slice
+  constexpr int kImgBytes = image_bytes<D, MK>() + 256;
+  constexpr int kRedBytes = ROT == TQ_ROT_DENSE ? 2 * KQ * kMaxG * D * 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t img[kImgBytes > kRedBytes ? kImgBytes : kRedBytes];
+  float* red = reinterpret_cast<float*>(img);
+  uint32_t* tail = reinterpret_cast<uint32_t*>(img + image_bytes<D, MK>());
+  __shared__ __attribute__((aligned(16))) float q_rot[kMaxG * D];
+  __shared__ __attribute__((aligned(16))) float q_sk[kMaxG * D];
+  __shared__ float coef_k[EXT ? 32 : 16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.cache.num_kv_heads;
+  const int G = a.num_q_heads / H;
+  const int s = blockIdx.x / H, hk = blockIdx.x % H;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
+  float* dst_raw = reinterpret_cast<float*>(dst + kImgBytes);  // EXT only
+  const bool qjl = !EXT || a.cache.codec.qjl;
+  if (tid < (EXT ? 32 : 16))
+    coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
+  if (a.cache.status != nullptr && hk == 0) check_sequence(a, s, tid, T);
+  const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
+  if constexpr (ROT == TQ_ROT_FWHT) {
+    if (wv < kMaxG) query_fwht<D, EXT>(a, qrow0, G, wv, lane, qjl, q_rot, q_sk, dst_raw);
+    __syncthreads();
+  } else {
+    // scores come out in base-2 logits: the softmax scale times log2(e) rides
+    // on both query operands, and the QJL constant sqrt(pi/2)/d on the sketch
+    // one.  qt and qh in one pass over q, from the transposed matrices Pi_K^T
+    // and (G Pi_K)^T: thread (i, k) sums slice k of the products for output
+    // coordinate i of the whole group, so that the threads of a wavefront read
+    // consecutive entries of a matrix row (each entry is read once); the
+    // slices meet in LDS.
+    const float s2 = a.scale * 1.4426950408889634f;
+    const float s2q = s2 * kQjlConst / float(D);
+    for (int i = tid; i < kMaxG * D; i += T) {
+      const int g = i / D;
+      q_rot[i] = g < G ? load_elem(a.q, a.q_dtype, qrow0 * D + i) : 0.f;
+      if constexpr (EXT) dst_raw[i] = q_rot[i] * s2;
+    }
+    __syncthreads();
+    constexpr int J = D / KQ;  // contraction slice per thread
+    const int i = tid % D, k = tid / D, k0 = k * J;
+    const float* m0 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 0)) + size_t(k0) * D + i;
+    const float* m1 = reinterpret_cast<const float*>(a.params + dense_t_offset(D, 1)) + size_t(k0) * D + i;
+    float ar[kMaxG] = {0.f, 0.f, 0.f, 0.f}, as[kMaxG] = {0.f, 0.f, 0.f, 0.f};
+    if (qjl) {
+#pragma unroll 16
+      for (int j = 0; j < J; ++j) {
+        const float u = m0[size_t(j) * D], v = m1[size_t(j) * D];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+          const float x = q_rot[h * D + k0 + j];
+          ar[h] = fmaf(u, x, ar[h]);
+          as[h] = fmaf(v, x, as[h]);
+        }
+      }
+    } else {
+#pragma unroll 16
+      for (int j = 0; j < J; ++j) {
+        const float u = m0[size_t(j) * D];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) ar[h] = fmaf(u, q_rot[h * D + k0 + j], ar[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      red[(k * kMaxG + h) * D + i] = ar[h];
+      red[((KQ + k) * kMaxG + h) * D + i] = as[h];
+    }
+    __syncthreads();
+    for (int o = tid; o < kMaxG * D; o += T) {
+      float vr = 0.f, vs = 0.f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        vr += red[q * kMaxG * D + o];
+        vs += red[(KQ + q) * kMaxG * D + o];
+      }
+      q_rot[o] = vr * s2;
+      q_sk[o] = vs * s2q;
+    }
+    __syncthreads();
+  }
+  if (wv < kMaxG) head_constants<D, MK, EXT>(q_rot, q_sk, coef_k, wv, lane, tail);
   __syncthreads();
-  for (int i = tid; i < (KP + 1) * KH * 128; i += T)
+  build_images<D, MK, EXT, T>(q_rot, q_sk, coef_k, tail, img, tid);
+  __syncthreads();
+  for (int i = tid; i < kImgBytes / 16; i += T)
     reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(img)[i];
 }
 
@@ -704,6 +737,18 @@ __host__ __device__ constexpr bool split_q_in_lds(int D, int MK, int BV, int fmt
   return split_occupancy(D, MK, BV, fmt) > 2 ? true : !split_fits(D, MK, BV, split_waves(D, MK, BV, fmt), false, fmt);
 }
 
+// With the FWHT rotation and few splits per (sequence, kv head) the split
+// work items build their query operands themselves: the transforms then cost
+// less than a launch and its workspace traffic.  With many splits per
+// (sequence, kv head) every one would repeat them, on SIMDs the score and
+// value work already keeps busy, so one preparation launch serves them all;
+// the dense rotation's products read two d x d matrices and always take that
+// launch.
+constexpr int kFusedQueryMaxSplits = 4;
+__host__ __device__ constexpr bool split_builds_query(int rot, int splits) {
+  return rot == TQ_ROT_FWHT && splits <= kFusedQueryMaxSplits;
+}
+
 // Re-base a head's reference maximum only when a block's maximum exceeds it by
 // more than this (weights stay below e^20; fp32 sums keep their range).
 constexpr float kRebase = 28.f;  // base-2 logits: weights stay below 2^28 of the reference
@@ -725,7 +770,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 //                       - sum_j 2^(j-1) sum_t p_t scale_{t,g} s_{j,t,c},  s = 1 - 2 bit,
 // the first two sums kept per (head, group) in registers; the result stays in
 // the value's own basis (no inverse rotation in the merge).
-template <int D, int MK, int BV, int NW, bool QL, int OCC, bool EXT, bool GV = false>
+template <int D, int MK, int BV, int NW, bool QL, int OCC, bool EXT, bool GV, bool FQ>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) void decode_split_kernel(DecodeArgs a, size_t part_offset) {
   static_assert(!GV || EXT, "group-quantized values are an extended format");
   constexpr int KP = num_planes(MK);   // key plane products
@@ -747,7 +792,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
 
   __shared__ __attribute__((aligned(16))) uint8_t w_img[GV ? NG * 2048 : 2048];   // softmax-weight operand(s)
   __shared__ float gsum[GV ? NW * kMaxG * NG * 2 : 1];  // GV: per-wavefront zero and scale sums
-  __shared__ __attribute__((aligned(16))) uint8_t q_img[QL ? (KP + 1) * KH * 2048 : 16];  // query operands
+  // query operands (FQ: with their tail, built here from the rotated queries and sketches)
+  __shared__ __attribute__((aligned(16))) uint8_t q_img[QL || FQ ? image_bytes<D, MK>() + (FQ ? 256 : 0) : 16];
+  __shared__ __attribute__((aligned(16))) float q_rs[FQ ? 2 * kMaxG * D : 1];
+  __shared__ float coef_k[FQ ? 32 : 1];
   __shared__ float red[NW][8];
   __shared__ float fin[NW][kMaxG];
   constexpr int kSideWords = 8;  // record stride in LDS: two words per lane group
@@ -790,25 +838,50 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     return;
   }
 
-  // query operands of this (sequence, kv head), lane-major images
-  const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
+  // query operands of this (sequence, kv head), lane-major images with their
+  // tail: built here (FQ) or read from the workspace
   const Codec& cd = cv.codec;
   const bool qjl = !EXT || cd.qjl;
   const int n_side = EXT ? cd.outliers : 0;          // sidecar entries per record
   const int side_words = EXT ? cd.side_bytes / 4 : 0;
-  if constexpr (EXT) {
-    if (n_side > 0) {
-      const float* src = reinterpret_cast<const float*>(qp + (KP + 1) * KH * 2048 + 256);
-      for (int i = tid; i < kMaxG * D; i += 64 * NW) q_raw[i] = src[i];
+  const uint8_t* qp;
+  if constexpr (FQ) {
+    // the plane coefficients, the heads' rotated queries and sketches (a
+    // wavefront per head), their constants, then the images
+    if (tid < (EXT ? 32 : 16))
+      coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
+    const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
+    float* q_sk = q_rs + kMaxG * D;
+    uint32_t* tail = reinterpret_cast<uint32_t*>(q_img + image_bytes<D, MK>());
+#pragma unroll
+    for (int i = 0; i < (kMaxG + NW - 1) / NW; ++i)
+      if (wvu + i * NW < kMaxG) query_fwht<D, EXT>(a, qrow0, G, wvu + i * NW, lane, qjl, q_rs, q_sk, q_raw);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (kMaxG + NW - 1) / NW; ++i)
+      if (wvu + i * NW < kMaxG) head_constants<D, MK, EXT>(q_rs, q_sk, coef_k, wvu + i * NW, lane, tail);
+    __syncthreads();
+    build_images<D, MK, EXT, 64 * NW>(q_rs, q_sk, coef_k, tail, q_img, tid);
+    __syncthreads();
+    qp = q_img;
+    if (cv.status != nullptr && hk == 0 && split == 0) check_sequence(a, s, tid, 64 * NW);
+  } else {
+    qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
+    if constexpr (EXT) {
+      if (n_side > 0) {
+        const float* src = reinterpret_cast<const float*>(qp + image_bytes<D, MK>() + 256);
+        for (int i = tid; i < kMaxG * D; i += 64 * NW) q_raw[i] = src[i];
+      }
+      if constexpr (!QL) __syncthreads();  // (with QL the operand images' barrier below covers it)
     }
-    if constexpr (!QL) __syncthreads();  // (with QL the operand images' barrier below covers it)
+    if constexpr (QL) {
+      for (int i = tid; i < image_bytes<D, MK>() / 16; i += 64 * NW)
+        reinterpret_cast<uint4*>(q_img)[i] = reinterpret_cast<const uint4*>(qp)[i];
+      __syncthreads();
+    }
   }
   v8i qa[QL ? 1 : KP + 1][QL ? 1 : KH];
-  if constexpr (QL) {
-    for (int i = tid; i < (KP + 1) * KH * 128; i += 64 * NW)
-      reinterpret_cast<uint4*>(q_img)[i] = reinterpret_cast<const uint4*>(qp)[i];
-    __syncthreads();
-  } else {
+  if constexpr (!QL) {
 #pragma unroll
     for (int pl = 0; pl <= KP; ++pl)
 #pragma unroll
@@ -831,7 +904,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   };
   // per-row operand scales of the query images (lane r16 scales row r16) and
   // the affine constants of head g4, which seed the score accumulators
-  const int32_t* tail_i = reinterpret_cast<const int32_t*>(qp + (KP + 1) * KH * 2048);
+  const int32_t* tail_i = reinterpret_cast<const int32_t*>(qp + image_bytes<D, MK>());
   const float* tail_f = reinterpret_cast<const float*>(tail_i + 16);
   const bool head_ok = g4 < G;
   const int sa = tail_i[r16];
@@ -1576,13 +1649,18 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
   constexpr bool QL = split_q_in_lds(D, MK, BV, FMT);
   constexpr int OCC = split_occupancy(D, MK, BV, FMT);
   const int H = a.cache.num_kv_heads;
-  hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(ROT == TQ_ROT_DENSE ? 1024 : 256),
-                     0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // one work item per (sequence, kv head, split), plus window_items per (sequence, kv head) for the window
-  hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT, GV>), dim3(a.num_seqs * H, a.splits + a.window_items),
-                     dim3(64 * NW), 0, st, a, part_offset);
+  const dim3 grid(a.num_seqs * H, a.splits + a.window_items);
+  hipError_t e;
+  if (ROT == TQ_ROT_FWHT && split_builds_query(ROT, a.splits)) {
+    hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT, GV, ROT == TQ_ROT_FWHT>), grid, dim3(64 * NW), 0, st,
+                       a, part_offset);
+  } else {
+    hipLaunchKernelGGL((decode_prep_kernel<D, MK, ROT, EXT>), dim3(a.num_seqs * H), dim3(prep_threads<ROT>()), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT, GV, false>), grid, dim3(64 * NW), 0, st, a, part_offset);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
