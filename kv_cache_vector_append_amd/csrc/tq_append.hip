@@ -760,6 +760,12 @@ struct DenseTile {
 // acc[ct][tt] (lane l, element i: coordinate q d/4 + 16 ct + 4 (l / 16) + i,
 // token 16 tt + l % 16).  A and B place K index 32 ks + 8 g + e at element e of
 // lane group g, so the pairing holds whatever the instruction's K order.
+// The matrix pieces are read through global-address-space pointers: a
+// uniform base plus a 32-bit lane offset and immediate offsets per K step, so
+// no 64-bit address arithmetic and no flat accesses (which would also count
+// against the LDS reads' waits).
+typedef const h8v __attribute__((address_space(1))) g_h8v;
+typedef const uint8_t __attribute__((address_space(1))) g_u8;
 template <int D>
 __device__ __forceinline__ void dense_gemm(const _Float16* mhi, const _Float16* mlo, const uint8_t* buf, int q,
                                            int lane, f4v (&acc)[DenseTile<D>::CT][4]) {
@@ -770,12 +776,15 @@ __device__ __forceinline__ void dense_gemm(const _Float16* mhi, const _Float16* 
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[ct][tt] = f4v{0.f, 0.f, 0.f, 0.f};
   h8v ah[2][DT::CT], al[2][DT::CT];
+  const g_u8* ghi = (const g_u8*)mhi;
+  const g_u8* glo = (const g_u8*)mlo;
+  const uint32_t lane_off = uint32_t(((q * DT::Q + r16) * D + 8 * g) * 2);
   auto load_a = [&](int ks, int slot) {
 #pragma unroll
     for (int ct = 0; ct < DT::CT; ++ct) {
-      const size_t off = size_t(q * DT::Q + 16 * ct + r16) * D + 32 * ks + 8 * g;
-      ah[slot][ct] = *reinterpret_cast<const h8v*>(mhi + off);
-      al[slot][ct] = *reinterpret_cast<const h8v*>(mlo + off);
+      const uint32_t off = lane_off + uint32_t((16 * ct * D + 32 * ks) * 2);
+      ah[slot][ct] = *reinterpret_cast<g_h8v*>(ghi + off);
+      al[slot][ct] = *reinterpret_cast<g_h8v*>(glo + off);
     }
   };
   load_a(0, 0);

@@ -1642,6 +1642,22 @@ __global__ __launch_bounds__(combine_threads<ROT>()) void decode_combine_kernel(
   }
 }
 
+constexpr int kSimds = 1024;  // 256 CUs x 4 SIMDs
+
+template <int D, int ROT>
+hipError_t launch_combine(const DecodeArgs& a, size_t part_offset, hipStream_t st) {
+  const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
+  if constexpr (ROT == TQ_ROT_FWHT) {
+    if (rows <= kWideCombineRows) {
+      hipLaunchKernelGGL((decode_combine_kernel<D, ROT, true>), dim3(rows), dim3(256), 0, st, a, part_offset);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_combine_kernel<D, ROT, false>), dim3((rows + rpb - 1) / rpb), dim3(combine_threads<ROT>()), 0, st, a,
+                     part_offset);
+  return hipGetLastError();
+}
+
 template <int D, int MK, int BV, int ROT, bool EXT, bool GV>
 hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) {
   constexpr int FMT = GV ? 2 : EXT ? 1 : 0;
@@ -1652,6 +1668,20 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
   // one work item per (sequence, kv head, split), plus window_items per (sequence, kv head) for the window
   const dim3 grid(a.num_seqs * H, a.splits + a.window_items);
   hipError_t e;
+  // Latency-bound launches (fewer wavefronts than SIMDs, FWHT): four
+  // wavefronts per work item, which build the query operands themselves, one
+  // query head each; every item's block then divides over four SIMDs.
+  constexpr bool kWideOk = ROT == TQ_ROT_FWHT && NW < 4 && split_shape_ok(D, 4);
+  if constexpr (kWideOk) {
+    if (size_t(grid.x) * grid.y * NW < size_t(kSimds)) {
+      constexpr bool QLW = !split_fits(D, MK, BV, 4, false, FMT);
+      hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, 4, QLW, OCC, EXT, GV, true>), grid, dim3(256), 0, st, a,
+                         part_offset);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_combine<D, ROT>(a, part_offset, st);
+    }
+  }
   if (ROT == TQ_ROT_FWHT && split_builds_query(ROT, a.splits)) {
     hipLaunchKernelGGL((decode_split_kernel<D, MK, BV, NW, QL, OCC, EXT, GV, ROT == TQ_ROT_FWHT>), grid, dim3(64 * NW), 0, st,
                        a, part_offset);
@@ -1663,16 +1693,7 @@ hipError_t launch_mfma(const DecodeArgs& a, size_t part_offset, hipStream_t st) 
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = a.num_seqs * a.num_q_heads, rpb = combine_rows<ROT>(0);
-  if constexpr (ROT == TQ_ROT_FWHT) {
-    if (rows <= kWideCombineRows) {
-      hipLaunchKernelGGL((decode_combine_kernel<D, ROT, true>), dim3(rows), dim3(256), 0, st, a, part_offset);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((decode_combine_kernel<D, ROT, false>), dim3((rows + rpb - 1) / rpb), dim3(combine_threads<ROT>()), 0, st, a,
-                     part_offset);
-  return hipGetLastError();
+  return launch_combine<D, ROT>(a, part_offset, st);
 }
 
 // Key and value bit counts the kernels are built for: the larger half's
@@ -1705,9 +1726,9 @@ int decode_mfma_items(const tq_config& cfg) {
   const Bits b = kernel_bits(cfg);
   const int d = cfg.head_dim;
   if (b.mk < 1 || b.mk > 4 || b.bv < 1 || b.bv > 4 || (d != 128 && d != 256)) return 2048;
-  // work items that fill every SIMD once: 1024 SIMDs x resident wavefronts / wavefronts per item
+  // work items that fill every SIMD once: SIMDs x resident wavefronts / wavefronts per item
   const int fmt = cfg.value_mode == TQ_VALUE_GROUP ? 2 : make_codec(cfg).ext ? 1 : 0;
-  return 1024 * split_occupancy(d, b.mk, b.bv, fmt) / split_waves(d, b.mk, b.bv, fmt);
+  return kSimds * split_occupancy(d, b.mk, b.bv, fmt) / split_waves(d, b.mk, b.bv, fmt);
 }
 
 size_t decode_prep_bytes(const tq_config& cfg, int num_seqs) {

@@ -54,14 +54,19 @@ CASES = {
     "group_values": ("group_values", [400, 3, 160, 0], 3),
     "group_values_dense_hd256": ("group_values_dense_hd256", [300, 77], 1),
     "every_feature_hd64_gqa8": ("every_feature_hd64_gqa8", [300, 130], 2),
-    # FWHT decode with at most four splits per (sequence, kv head), where the
-    # split work items build their query operands themselves, and with more,
-    # where a preparation launch builds them: each format on both sides
+    # FWHT decode, where the query operands come from three places: with few
+    # (sequence, kv head) units the launch has fewer wavefronts than SIMDs and
+    # takes four wavefronts per work item that build them (the small cases
+    # above and these two); with many units and at most four splits each the
+    # split work items build them; with more splits a preparation launch does
     "mixed_3p5_2p5_fewsplits": ("mixed_3p5_2p5", [500, 129, 300], 2),
     "scaled_unbiased_3p5_3_fewsplits": ("scaled_unbiased_3p5_3", [500, 33, 257], 2),
     "outlier_sidecar_fewsplits": ("outlier_sidecar", [500, 260, 1], 1),
     "group_values_manysplits": ("group_values", [1000, 3, 160, 0], 3),
     "hd256_fwht_3_2_manysplits": ("hd256_long_fwht_3_2", [1100, 31], 1),
+    "gqa_decode_manyunits": ("gqa_decode", [800] + _ragged(39, 200, 160), 1),
+    "mixed_3p5_2p5_manyunits": ("mixed_3p5_2p5", [800] + _ragged(39, 200, 160), 1),
+    "group_values_manyunits": ("group_values", [800] + _ragged(39, 200, 160), 1),
 }
 
 import workloads as _w
