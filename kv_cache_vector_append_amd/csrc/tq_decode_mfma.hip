@@ -232,55 +232,65 @@ __host__ __device__ constexpr int image_bytes() { return (num_planes(MK) + 1) * 
 // log2(e), and the sketch also the QJL constant sqrt(pi/2)/d), to LDS rows
 // q_rot[h] and q_sk[h]: zeros past the group, and no sketch for keys without
 // the QJL plane.  EXT also keeps the unrotated query in logit units in raw[h]
-// for the sidecar entries.  One wavefront per head.
-template <int D, bool EXT>
-__device__ __forceinline__ void query_fwht(const DecodeArgs& a, size_t qrow0, int G, int h, int lane, bool qjl,
-                                           float* q_rot, float* q_sk, float* raw) {
+// for the sidecar entries.  One wavefront per head, in two steps: the loads
+// (query row and the three sign masks), then the transforms, so that a
+// caller can issue other loads in between.
+template <int D>
+struct QueryRegs {
+  float x[D / 64];
+  uint32_t sgk[D / 64], sg1[D / 64], sg2[D / 64];
+};
+template <int D>
+__device__ __forceinline__ void query_load(const DecodeArgs& a, size_t qrow0, int G, int h, int lane, QueryRegs<D>& q) {
   constexpr int R = D / 64;
-  const float s2 = a.scale * 1.4426950408889634f;
-  const float s2q = s2 * kQjlConst / float(D);
-  // every global load first (one uniform dtype branch), so that they are in
-  // flight together
-  float x[R], y[R];
-  uint32_t sgk[R], sg1[R], sg2[R];
   const size_t qb = (qrow0 + h) * D + lane;
+  // one uniform dtype branch, every load in flight together
   if (h >= G) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = 0.f;
+    for (int r = 0; r < R; ++r) q.x[r] = 0.f;
   } else if (a.q_dtype == TQ_F32) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = static_cast<const float*>(a.q)[qb + r * 64];
+    for (int r = 0; r < R; ++r) q.x[r] = static_cast<const float*>(a.q)[qb + r * 64];
   } else {
     uint16_t qbits[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) qbits[r] = static_cast<const uint16_t*>(a.q)[qb + r * 64];
     const bool bf = a.q_dtype == TQ_BF16;
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = bf ? bf16_bits_to_float(qbits[r]) : f16_bits_to_float(qbits[r]);
+    for (int r = 0; r < R; ++r) q.x[r] = bf ? bf16_bits_to_float(qbits[r]) : f16_bits_to_float(qbits[r]);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int c = r * 64 + lane;
-    sgk[r] = sign_bit(a.params, kRoleKeyRot, c);
-    sg1[r] = sign_bit(a.params, kRoleSketch1, c);
-    sg2[r] = sign_bit(a.params, kRoleSketch2, c);
+    q.sgk[r] = sign_bit(a.params, kRoleKeyRot, c);
+    q.sg1[r] = sign_bit(a.params, kRoleSketch1, c);
+    q.sg2[r] = sign_bit(a.params, kRoleSketch2, c);
   }
+}
+template <int D, bool EXT>
+__device__ __forceinline__ void query_finish(const DecodeArgs& a, QueryRegs<D>& q, int h, int lane, bool qjl, float* q_rot,
+                                             float* q_sk, float* raw) {
+  constexpr int R = D / 64;
+  const float s2 = a.scale * 1.4426950408889634f;
+  const float s2q = s2 * kQjlConst / float(D);
+  float* x = q.x;
+  float y[R];
   if constexpr (EXT) {
 #pragma unroll
     for (int r = 0; r < R; ++r) raw[h * D + r * 64 + lane] = x[r] * s2;
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], sgk[r]);
-  wave_fwht<R>(x, lane);
+  for (int r = 0; r < R; ++r) x[r] = apply_sign(x[r], q.sgk[r]);
+  wave_fwht<R>(q.x, lane);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     x[r] *= rsqrtf(float(D));
-    y[r] = apply_sign(x[r], sg1[r]);
+    y[r] = apply_sign(x[r], q.sg1[r]);
   }
   if (qjl) {
     wave_fwht<R>(y, lane);
 #pragma unroll
-    for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), sg2[r]);
+    for (int r = 0; r < R; ++r) y[r] = apply_sign(y[r] * rsqrtf(float(D)), q.sg2[r]);
     wave_fwht<R>(y, lane);
   } else {
 #pragma unroll
@@ -291,6 +301,13 @@ __device__ __forceinline__ void query_fwht(const DecodeArgs& a, size_t qrow0, in
     q_rot[h * D + r * 64 + lane] = x[r] * s2;
     q_sk[h * D + r * 64 + lane] = y[r] * s2q;
   }
+}
+template <int D, bool EXT>
+__device__ __forceinline__ void query_fwht(const DecodeArgs& a, size_t qrow0, int G, int h, int lane, bool qjl,
+                                           float* q_rot, float* q_sk, float* raw) {
+  QueryRegs<D> q;
+  query_load<D>(a, qrow0, G, h, lane, q);
+  query_finish<D, EXT>(a, q, h, lane, qjl, q_rot, q_sk, raw);
 }
 
 // Head h's operand constants (one wavefront): one power of two 2^e bringing
@@ -844,54 +861,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
   const bool qjl = !EXT || cd.qjl;
   const int n_side = EXT ? cd.outliers : 0;          // sidecar entries per record
   const int side_words = EXT ? cd.side_bytes / 4 : 0;
+  // FQ: the group's query rows, sign masks and plane coefficients are
+  // requested here, the first block's pages after them, and the operands are
+  // built while the pages are in flight (a wavefront per head)
+  constexpr int HPW = (kMaxG + NW - 1) / NW;  // query heads per wavefront
+  QueryRegs<D> qreg[FQ ? HPW : 1];
+  float coef_r = 0.f;
   const uint8_t* qp;
   if constexpr (FQ) {
-    // the plane coefficients, the heads' rotated queries and sketches (a
-    // wavefront per head), their constants, then the images
-    if (tid < (EXT ? 32 : 16))
-      coef_k[tid] = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
     const size_t qrow0 = size_t(s) * a.num_q_heads + size_t(hk) * G;
-    float* q_sk = q_rs + kMaxG * D;
-    uint32_t* tail = reinterpret_cast<uint32_t*>(q_img + image_bytes<D, MK>());
+    if (tid < (EXT ? 32 : 16))
+      coef_r = reinterpret_cast<const float*>(a.params + kOffKeyPlaneCoef + (tid >= 16 ? kOffUpperHalf : 0))[tid % 16];
 #pragma unroll
-    for (int i = 0; i < (kMaxG + NW - 1) / NW; ++i)
-      if (wvu + i * NW < kMaxG) query_fwht<D, EXT>(a, qrow0, G, wvu + i * NW, lane, qjl, q_rs, q_sk, q_raw);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < (kMaxG + NW - 1) / NW; ++i)
-      if (wvu + i * NW < kMaxG) head_constants<D, MK, EXT>(q_rs, q_sk, coef_k, wvu + i * NW, lane, tail);
-    __syncthreads();
-    build_images<D, MK, EXT, 64 * NW>(q_rs, q_sk, coef_k, tail, q_img, tid);
-    __syncthreads();
+    for (int i = 0; i < HPW; ++i)
+      if (wvu + i * NW < kMaxG) query_load<D>(a, qrow0, G, wvu + i * NW, lane, qreg[i]);
     qp = q_img;
-    if (cv.status != nullptr && hk == 0 && split == 0) check_sequence(a, s, tid, 64 * NW);
   } else {
     qp = reinterpret_cast<const uint8_t*>(a.workspace) + size_t(blockIdx.x) * prep_stride(D, MK, EXT);
-    if constexpr (EXT) {
-      if (n_side > 0) {
-        const float* src = reinterpret_cast<const float*>(qp + image_bytes<D, MK>() + 256);
-        for (int i = tid; i < kMaxG * D; i += 64 * NW) q_raw[i] = src[i];
-      }
-      if constexpr (!QL) __syncthreads();  // (with QL the operand images' barrier below covers it)
-    }
-    if constexpr (QL) {
-      for (int i = tid; i < image_bytes<D, MK>() / 16; i += 64 * NW)
-        reinterpret_cast<uint4*>(q_img)[i] = reinterpret_cast<const uint4*>(qp)[i];
-      __syncthreads();
-    }
   }
   v8i qa[QL ? 1 : KP + 1][QL ? 1 : KH];
-  if constexpr (!QL) {
-#pragma unroll
-    for (int pl = 0; pl <= KP; ++pl)
-#pragma unroll
-      for (int hf = 0; hf < KH; ++hf) {
-        const uint8_t* img = qp + (pl * KH + hf) * 2048;
-        const uint4 lo = reinterpret_cast<const uint4*>(img)[lane];
-        const uint4 hi = reinterpret_cast<const uint4*>(img + 1024)[lane];
-        qa[pl][hf] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-      }
-  }
   auto qop = [&](int pl, int hf) -> v8i {
     if constexpr (QL) {
       const uint8_t* img = q_img + (pl * KH + hf) * 2048;
@@ -903,12 +891,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     }
   };
   // per-row operand scales of the query images (lane r16 scales row r16) and
-  // the affine constants of head g4, which seed the score accumulators
-  const int32_t* tail_i = reinterpret_cast<const int32_t*>(qp + image_bytes<D, MK>());
-  const float* tail_f = reinterpret_cast<const float*>(tail_i + 16);
+  // the affine constants of head g4, which seed the score accumulators (read
+  // once the operands are in place)
   const bool head_ok = g4 < G;
-  const int sa = tail_i[r16];
-  const float k_m = tail_f[g4], k_q = tail_f[kMaxG + g4];
+  int sa = 0;
+  float k_m = 0.f, k_q = 0.f;
 
   // page addressing: uniform page base + constant per-lane offsets.  Page ids
   // come through the scalar data cache (uniform addresses in the constant
@@ -1092,6 +1079,54 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC))) 
     fetch_ids(t_begin);
     load_keys();
     load_values();
+  }
+  // the query operands, while the first block's pages are in flight (the
+  // barriers wait for LDS traffic only)
+  if constexpr (FQ) {
+    if (tid < (EXT ? 32 : 16)) coef_k[tid] = coef_r;
+    float* q_sk = q_rs + kMaxG * D;
+    uint32_t* tail = reinterpret_cast<uint32_t*>(q_img + image_bytes<D, MK>());
+#pragma unroll
+    for (int i = 0; i < HPW; ++i)
+      if (wvu + i * NW < kMaxG) query_finish<D, EXT>(a, qreg[i], wvu + i * NW, lane, qjl, q_rs, q_sk, q_raw);
+    block_sync<NW>();
+#pragma unroll
+    for (int i = 0; i < HPW; ++i)
+      if (wvu + i * NW < kMaxG) head_constants<D, MK, EXT>(q_rs, q_sk, coef_k, wvu + i * NW, lane, tail);
+    block_sync<NW>();
+    build_images<D, MK, EXT, 64 * NW>(q_rs, q_sk, coef_k, tail, q_img, tid);
+    block_sync<NW>();
+    if (cv.status != nullptr && hk == 0 && split == 0) check_sequence(a, s, tid, 64 * NW);
+  } else {
+    if constexpr (EXT) {
+      if (n_side > 0) {
+        const float* src = reinterpret_cast<const float*>(qp + image_bytes<D, MK>() + 256);
+        for (int i = tid; i < kMaxG * D; i += 64 * NW) q_raw[i] = src[i];
+      }
+    }
+    if constexpr (QL) {
+      for (int i = tid; i < image_bytes<D, MK>() / 16; i += 64 * NW)
+        reinterpret_cast<uint4*>(q_img)[i] = reinterpret_cast<const uint4*>(qp)[i];
+    }
+    if constexpr (QL || EXT) __syncthreads();
+  }
+  if constexpr (!QL) {
+#pragma unroll
+    for (int pl = 0; pl <= KP; ++pl)
+#pragma unroll
+      for (int hf = 0; hf < KH; ++hf) {
+        const uint8_t* img = qp + (pl * KH + hf) * 2048;
+        const uint4 lo = reinterpret_cast<const uint4*>(img)[lane];
+        const uint4 hi = reinterpret_cast<const uint4*>(img + 1024)[lane];
+        qa[pl][hf] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+  }
+  {
+    const int32_t* tail_i = reinterpret_cast<const int32_t*>(qp + image_bytes<D, MK>());
+    const float* tail_f = reinterpret_cast<const float*>(tail_i + 16);
+    sa = tail_i[r16];
+    k_m = tail_f[g4];
+    k_q = tail_f[kMaxG + g4];
   }
   // wait here once for everything requested so far, so that the loop's own
   // waits only ever cover loads issued inside the loop
