@@ -111,12 +111,16 @@ SOURCES = {
     "append": [_CSRC + f for f in ("tq_append.hip", "tq_device.h", "tq_internal.h")],
 }
 KERNELS = {
-    "decode": "tq_decode_attention (decode_prep + decode_split + decode_combine)",
+    "decode": "tq_decode_attention (decode_split + decode_combine, after decode_prep where that launch builds "
+              "the query operands)",
     "append": "tq_quantize_append (append_tok_kernel, append_dense_kernel or append_kernel)",
 }
-# rocprofv3 kernel names of each call's kernels (an append launches one of the two)
+# rocprofv3 kernel names of each call's kernels (an append launches one of the
+# alternatives); groups in OPTIONAL_KERNELS may be absent (the split work items
+# build the query operands themselves)
 KERNEL_MATCH = {"decode": (("decode_prep_kernel",), ("decode_split_kernel",), ("decode_combine_kernel",)),
                 "append": (("append_tok_kernel", "append_dense_kernel", "append_kernel<"),)}
+OPTIONAL_KERNELS = {("decode_prep_kernel",)}
 CALIBRATION_BYTES = 1 << 30
 
 
@@ -180,7 +184,9 @@ def write_traffic(fetch_csv, write_csv, workload):
             if fv and wv:
                 fl, wl = fv[-TRAFFIC_LAST_DISPATCHES:], wv[-TRAFFIC_LAST_DISPATCHES:]
                 per_kernel[fl[-1][2]] = (float(np.median([v for _, v, _ in fl])), float(np.median([v for _, v, _ in wl])))
-        if len(per_kernel) != len(groups) or not f_scale or not w_scale:
+        required = [g for g in groups if g not in OPTIONAL_KERNELS]
+        found = {n for alts in groups for n in alts if any(n in k for k in per_kernel)}
+        if any(not any(n in found for n in alts) for alts in required) or not f_scale or not w_scale:
             continue
         fb = sum(v[0] for v in per_kernel.values()) * f_scale
         wb = sum(v[1] for v in per_kernel.values()) * w_scale
