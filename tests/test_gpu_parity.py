@@ -54,11 +54,14 @@ CASES = {
     "group_values": ("group_values", [400, 3, 160, 0], 3),
     "group_values_dense_hd256": ("group_values_dense_hd256", [300, 77], 1),
     "every_feature_hd64_gqa8": ("every_feature_hd64_gqa8", [300, 130], 2),
-    # FWHT decode, where the query operands come from three places: with few
-    # (sequence, kv head) units the launch has fewer wavefronts than SIMDs and
-    # takes four wavefronts per work item that build them (the small cases
-    # above and these two); with many units and at most four splits each the
-    # split work items build them; with more splits a preparation launch does
+    # FWHT decode, where the query operands come from three places: a launch
+    # whose narrow kernel (one or two wavefronts per work item) would have
+    # fewer wavefronts than the GPU has SIMDs takes four wavefronts per item
+    # that build them (most small cases, among them mixed_3p5_2p5_fewsplits and
+    # the two manysplits cases); otherwise the split work items build them when
+    # a (sequence, kv head) has at most four splits (scaled_unbiased and
+    # outlier_sidecar fewsplits, whose kernels have four wavefronts), and a
+    # preparation launch does with more (the manyunits cases, outlier_stress)
     "mixed_3p5_2p5_fewsplits": ("mixed_3p5_2p5", [500, 129, 300], 2),
     "scaled_unbiased_3p5_3_fewsplits": ("scaled_unbiased_3p5_3", [500, 33, 257], 2),
     "outlier_sidecar_fewsplits": ("outlier_sidecar", [500, 260, 1], 1),
