@@ -124,6 +124,39 @@ OPTIONAL_KERNELS = {("decode_prep_kernel",)}
 CALIBRATION_BYTES = 1 << 30
 
 
+def hbm_reference():
+    """Streaming rates plain torch kernels reach on this GPU in the same run, as
+    context for the decode's rate: a read-only reduction and an elementwise
+    read + write pass over four rotating 1 GiB fp32 buffers (so that no pass
+    finds its data in the last-level cache), each timed with one event pair
+    over 8 passes after 2 untimed ones."""
+    import torch
+    n = CALIBRATION_BYTES // 4
+    bufs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    acc = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def rate(fn, bytes_per_pass):
+        for i in range(2):
+            fn(bufs[i % 4])
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(8):
+            fn(bufs[(i + 2) % 4])
+        e.record()
+        e.synchronize()
+        return bytes_per_pass * 8 / (s.elapsed_time(e) / 1e3) / 1e9
+
+    read = rate(lambda b: torch.sum(b, dim=0, out=acc), CALIBRATION_BYTES)
+    read_write = rate(lambda b: torch.neg(b, out=out), 2 * CALIBRATION_BYTES)
+    del bufs, out, acc
+    torch.cuda.empty_cache()
+    return {"read_GBs": round(read, 1), "read_write_GBs": round(read_write, 1),
+            "method": "torch.sum (read) and torch.neg (read + write) over four rotating 1 GiB fp32 buffers, "
+                      "8 timed passes each"}
+
+
 def calibration_copy():
     """One plain device-to-device copy of CALIBRATION_BYTES (read once, written
     once), whose FETCH_SIZE / WRITE_SIZE calibrate the counters' units."""
@@ -616,6 +649,12 @@ def main(argv=None):
     if w.name in QUALITY_HEAD and not args.calibrate_copy:
         line["quality_vs_exact"] = quality_vs_exact(w, r["setup"])
     del r
+    if not args.calibrate_copy:
+        ref = hbm_reference()
+        dec_rate = calls["decode"]["bytes"] / (calls["decode"]["ms"] / 1e3) / 1e9
+        ref["decode_frac_of_read"] = round(dec_rate / ref["read_GBs"], 4)
+        ref["decode_frac_of_read_write"] = round(dec_rate / ref["read_write_GBs"], 4)
+        line["hbm_reference"] = ref
     if not args.no_extra:
         import torch
         extra = {}
