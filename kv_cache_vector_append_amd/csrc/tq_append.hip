@@ -766,15 +766,45 @@ struct DenseTile {
 // against the LDS reads' waits).
 typedef const h8v __attribute__((address_space(1))) g_h8v;
 typedef const uint8_t __attribute__((address_space(1))) g_u8;
-template <int D>
+// ONE: only 16-token tile tt0 holds new tokens (short appends), so only its
+// products are formed; the other tiles' outputs are zero.
+template <int D, bool ONE = false>
 __device__ __forceinline__ void dense_gemm(const _Float16* mhi, const _Float16* mlo, const uint8_t* buf, int q,
-                                           int lane, f4v (&acc)[DenseTile<D>::CT][4]) {
+                                           int lane, f4v (&acc)[DenseTile<D>::CT][4], int tt0 = 0) {
   using DT = DenseTile<D>;
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int ct = 0; ct < DT::CT; ++ct)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[ct][tt] = f4v{0.f, 0.f, 0.f, 0.f};
+  if constexpr (ONE) {
+    f4v a1[DT::CT];
+#pragma unroll
+    for (int ct = 0; ct < DT::CT; ++ct) a1[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    const g_u8* ghi = (const g_u8*)mhi;
+    const g_u8* glo = (const g_u8*)mlo;
+    const uint32_t lane_off = uint32_t(((q * DT::Q + r16) * D + 8 * g) * 2);
+    const uint8_t* brow = buf + (16 * tt0 + r16) * DT::ROWB;
+#pragma unroll
+    for (int ks = 0; ks < DT::KS; ++ks) {
+      const h8v bh = *reinterpret_cast<const h8v*>(brow + (4 * ks + g) * 32);
+      const h8v bl = *reinterpret_cast<const h8v*>(brow + (4 * ks + g) * 32 + 16);
+#pragma unroll
+      for (int ct = 0; ct < DT::CT; ++ct) {
+        const uint32_t off = lane_off + uint32_t((16 * ct * D + 32 * ks) * 2);
+        const h8v ah = *reinterpret_cast<g_h8v*>(ghi + off), al = *reinterpret_cast<g_h8v*>(glo + off);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, a1[ct], 0, 0, 0);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, a1[ct], 0, 0, 0);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, a1[ct], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < DT::CT; ++ct)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        if (tt == tt0) acc[ct][tt] = a1[ct];
+    return;
+  }
   h8v ah[2][DT::CT], al[2][DT::CT];
   const g_u8* ghi = (const g_u8*)mhi;
   const g_u8* glo = (const g_u8*)mlo;
@@ -846,7 +876,11 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int D, int MK, int BV>
+// SHORT (appends of at most 16 tokens per sequence, such as decode steps):
+// a chunk whose new tokens fall in one 16-token tile forms only that tile's
+// products.  (A separate instantiation: the extra path in the long-append
+// kernel cost it 3%.)
+template <int D, int MK, int BV, bool SHORT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void append_dense_kernel(AppendArgs a) {
   using DT = DenseTile<D>;
   constexpr int P = 16, T = DT::T, Q = DT::Q, LPT = D / 8, TPP = 64 / LPT;
@@ -970,10 +1004,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (sub == 0) nrm[t] = valid && nu >= kZeroNorm ? nu : 0.f;
       }
     };
+    // SHORT: the 16-token tiles of this chunk that hold new tokens
+    const int tt_first = max(start - P0, 0) / 16, tt_last = (min(new_len - P0, T) - 1) / 16;
     auto gemm_to_rows = [&](int m) {
       f4v acc[DT::CT][4];
       block_barrier();  // rows staged
-      dense_gemm<D>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc);
+      if (SHORT && tt_first == tt_last)
+        dense_gemm<D, SHORT>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc, tt_first);
+      else
+        dense_gemm<D>(m16 + size_t(m) * 2 * mm, m16 + size_t(m) * 2 * mm + mm, buf, q, lane, acc);
       block_barrier();  // every wavefront has read the rows
       dense_store<D>(acc, buf, q, lane);
       block_barrier();  // products visible
@@ -1129,23 +1168,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 template <int D, int MK>
-hipError_t launch_dense_bv(const AppendArgs& a, int units, hipStream_t st) {
+hipError_t launch_dense_bv(const AppendArgs& a, int units, hipStream_t st, bool short_append) {
+#define TQ_DENSE(BV_)                                                                                   \
+  case BV_:                                                                                             \
+    if (short_append) hipLaunchKernelGGL((append_dense_kernel<D, MK, BV_, true>), dim3(units), dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((append_dense_kernel<D, MK, BV_, false>), dim3(units), dim3(256), 0, st, a); \
+    break;
   switch (a.value_bits) {
-    case 1: hipLaunchKernelGGL((append_dense_kernel<D, MK, 1>), dim3(units), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((append_dense_kernel<D, MK, 2>), dim3(units), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((append_dense_kernel<D, MK, 3>), dim3(units), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((append_dense_kernel<D, MK, 4>), dim3(units), dim3(256), 0, st, a); break;
+    TQ_DENSE(1) TQ_DENSE(2) TQ_DENSE(3) TQ_DENSE(4)
     default: return hipErrorInvalidValue;
   }
+#undef TQ_DENSE
   return hipGetLastError();
 }
 
+// appends of at most this many tokens per sequence take the SHORT kernel
+constexpr int kDenseShortMaxNew = 16;
+
 template <int D>
-hipError_t launch_dense(const AppendArgs& a, int units, hipStream_t st) {
+hipError_t launch_dense(const AppendArgs& a, int units, hipStream_t st, int max_new) {
+  const bool short_append = max_new <= kDenseShortMaxNew;
   switch (a.key_mse_bits) {
-    case 1: return launch_dense_bv<D, 1>(a, units, st);
-    case 2: return launch_dense_bv<D, 2>(a, units, st);
-    case 3: return launch_dense_bv<D, 3>(a, units, st);
+    case 1: return launch_dense_bv<D, 1>(a, units, st, short_append);
+    case 2: return launch_dense_bv<D, 2>(a, units, st, short_append);
+    case 3: return launch_dense_bv<D, 3>(a, units, st, short_append);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1201,7 +1247,8 @@ int launch_append(const tq_config& cfg, const AppendArgs& args, int num_seqs, in
     a.parts = (max_new + 63) / 64 + 1;
     const long long units = (long long)num_seqs * H * a.parts;
     if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-    return cfg.head_dim == 128 ? launch_dense<128>(a, int(units), st) : launch_dense<256>(a, int(units), st);
+    return cfg.head_dim == 128 ? launch_dense<128>(a, int(units), st, max_new)
+                               : launch_dense<256>(a, int(units), st, max_new);
   }
   if (!dense && (cfg.head_dim == 64 || cfg.head_dim == 128) && max_new >= kTokenLaneMinNew) {
     // token-per-lane kernel: one wavefront per 64-position chunk a sequence's new tokens touch
