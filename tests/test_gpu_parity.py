@@ -67,6 +67,8 @@ CASES = {
     "outlier_sidecar_fewsplits": ("outlier_sidecar", [500, 260, 1], 1),
     "group_values_manysplits": ("group_values", [1000, 3, 160, 0], 3),
     "hd256_fwht_3_2_manysplits": ("hd256_long_fwht_3_2", [1100, 31], 1),
+    # dense rotation with fp32 inputs
+    "dense_f32_inputs": ("dense_f32_hd256", [300, 77], 1),
     "gqa_decode_manyunits": ("gqa_decode", [800] + _ragged(39, 200, 160), 1),
     "mixed_3p5_2p5_manyunits": ("mixed_3p5_2p5", [800] + _ragged(39, 200, 160), 1),
     "group_values_manyunits": ("group_values", [800] + _ragged(39, 200, 160), 1),
@@ -91,6 +93,7 @@ _w.WORKLOADS.setdefault("scaled_mse_dense_hd256", _w.HD256_DENSE_32.replace(
     name="scaled_mse_dense_hd256", key_mode="scaled_mse", key_bits=2, value_bits=2))
 _w.WORKLOADS.setdefault("group_values_dense_hd256", _w.HD256_DENSE_44.replace(
     name="group_values_dense_hd256", value_mode="group"))
+_w.WORKLOADS.setdefault("dense_f32_hd256", _w.HD256_DENSE_32.replace(name="dense_f32_hd256", input_dtype="f32"))
 _w.WORKLOADS.setdefault("every_feature_hd64_gqa8", _w.GQA_DECODE.replace(
     name="every_feature_hd64_gqa8", num_q_heads=16, num_kv_heads=2, head_dim=64, key_mode="scaled_unbiased",
     key_bits=2, key_bits_hi=3, value_mode="group", value_bits=2, value_bits_hi=3, key_outliers=3, window=32,
