@@ -785,18 +785,35 @@ __device__ __forceinline__ void dense_gemm(const _Float16* mhi, const _Float16* 
     const g_u8* glo = (const g_u8*)mlo;
     const uint32_t lane_off = uint32_t(((q * DT::Q + r16) * D + 8 * g) * 2);
     const uint8_t* brow = buf + (16 * tt0 + r16) * DT::ROWB;
+    // the matrix pieces of NB K steps in flight: each step's slot is refilled
+    // with step ks + NB once its products are issued (the scheduling barriers
+    // keep the compiler from moving the loads next to their first use, which
+    // would wait out one memory round trip per K step)
+    constexpr int NB = DT::KS < 3 ? DT::KS : 3;
+    h8v ah[NB][DT::CT], al[NB][DT::CT];
+    auto load_a = [&](int ks) {
+#pragma unroll
+      for (int ct = 0; ct < DT::CT; ++ct) {
+        const uint32_t off = lane_off + uint32_t((16 * ct * D + 32 * ks) * 2);
+        ah[ks % NB][ct] = *reinterpret_cast<g_h8v*>(ghi + off);
+        al[ks % NB][ct] = *reinterpret_cast<g_h8v*>(glo + off);
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks) load_a(ks);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < DT::KS; ++ks) {
       const h8v bh = *reinterpret_cast<const h8v*>(brow + (4 * ks + g) * 32);
       const h8v bl = *reinterpret_cast<const h8v*>(brow + (4 * ks + g) * 32 + 16);
 #pragma unroll
       for (int ct = 0; ct < DT::CT; ++ct) {
-        const uint32_t off = lane_off + uint32_t((16 * ct * D + 32 * ks) * 2);
-        const h8v ah = *reinterpret_cast<g_h8v*>(ghi + off), al = *reinterpret_cast<g_h8v*>(glo + off);
-        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, a1[ct], 0, 0, 0);
-        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, a1[ct], 0, 0, 0);
-        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, a1[ct], 0, 0, 0);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks % NB][ct], bh, a1[ct], 0, 0, 0);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks % NB][ct], bl, a1[ct], 0, 0, 0);
+        a1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks % NB][ct], bh, a1[ct], 0, 0, 0);
       }
+      if (ks + NB < DT::KS) load_a(ks + NB);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int ct = 0; ct < DT::CT; ++ct)
