@@ -75,13 +75,72 @@ __device__ __forceinline__ void rotate_dense_t(float (&x)[D / 64], const float* 
   asm volatile("" ::: "memory");
 }
 
+// The value of lane l ^ S (every lane active): DPP moves inside each row of
+// 16 lanes below S = 16 (xor 4 = half-row mirror, then quad reversal; xor 8 =
+// row mirror, then half-row mirror), the LDS crossbar at 16 and 32.  A chain
+// of such exchanges (the transforms and sums of one token) then waits on the
+// crossbar only for its last two steps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int S>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (S == 1) return dpp_mov<0xB1>(v);
+  else if constexpr (S == 2) return dpp_mov<0x4E>(v);
+  else if constexpr (S == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+  else if constexpr (S == 8) return dpp_mov<0x141>(dpp_mov<0x140>(v));
+  else return __shfl_xor(v, S);
+}
+// sum over the wavefront, pairs combined in the order of wave_sum
+__device__ __forceinline__ float wave_sum_x(float v) {
+  v += lane_xor<32>(v);
+  v += lane_xor<16>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<1>(v);
+  return v;
+}
+// one butterfly stage of wave_fwht (half-width S across lanes)
+template <int S, int R>
+__device__ __forceinline__ void fwht_stage(float (&v)[R], int lane) {
+  const bool upper = (lane & S) != 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float p = lane_xor<S>(v[r]);
+    v[r] = upper ? (p - v[r]) : (v[r] + p);
+  }
+}
+// wave_fwht with the exchanges above (the same butterflies in the same order)
+template <int R>
+__device__ __forceinline__ void wave_fwht_x(float (&v)[R], int lane) {
+  fwht_stage<1>(v, lane);
+  fwht_stage<2>(v, lane);
+  fwht_stage<4>(v, lane);
+  fwht_stage<8>(v, lane);
+  fwht_stage<16>(v, lane);
+  fwht_stage<32>(v, lane);
+#pragma unroll
+  for (int s = 1; s < R; s <<= 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!(r & s)) {
+        const float x = v[r], y = v[r + s];
+        v[r] = x + y;
+        v[r + s] = x - y;
+      }
+    }
+  }
+}
+
 // FWHT rotation with the role's sign bits already in registers (as masks on
 // the float sign bit): x <- scale * H D x.
 template <int R>
 __device__ __forceinline__ void fwht_rotate(float (&x)[R], const uint32_t (&sm)[R], int lane, float scale) {
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] = __uint_as_float(__float_as_uint(x[r]) ^ sm[r]);
-  wave_fwht<R>(x, lane);
+  wave_fwht_x<R>(x, lane);
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] *= scale;
 }
@@ -196,7 +255,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
         x[r] = xin[r];
         ss = fmaf(x[r], x[r], ss);
       }
-      ss = wave_sum(ss);
+      ss = wave_sum_x(ss);
       const float nu = sqrtf(ss);
       const bool zero = !(nu >= kZeroNorm);
       const float inv = zero ? 0.f : 1.0f / nu;
@@ -216,7 +275,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
           e[r] = zero ? 0.f : x[r] - c;
           es = fmaf(e[r], e[r], es);
         }
-        es = wave_sum(es);
+        es = wave_sum_x(es);
         const float gamma = sqrtf(es);
         // QJL projection w = S e: FWHT variant S = H D2 H_n D1, dense variant S = G
         if constexpr (ROT == TQ_ROT_FWHT) {
